@@ -1,0 +1,17 @@
+"""Diagonal-aware sparse attention for autoregressive image generation on
+MI355X (gfx950): HIP kernels behind the C ABI in include/diagattn.h, with a
+thin torch binding for device memory and streams.
+"""
+from ._native import DiagAttnError, load  # noqa: F401
+from .api import (  # noqa: F401
+    BAND,
+    DENSE,
+    ROWDIAG,
+    decode_workspace_bytes,
+    keep_cap,
+    keep_count,
+    keepset_build,
+    kv_cache,
+    mask,
+    sparse_decode_attn,
+)

@@ -1,0 +1,140 @@
+"""Python binding of libdiagattn: argument marshalling only.
+
+Each function takes torch tensors that live on the GPU, passes their
+pointers and the current HIP stream to the C entry point of the same name
+(``da_<name>`` in include/diagattn.h) and returns the output tensors.
+PyTorch supplies device memory and streams; every step of the computation
+runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from ._native import DaKvCache, DaMask, check, load
+
+DENSE, BAND, ROWDIAG = 0, 1, 2
+_DTYPE = {torch.float32: 0, torch.bfloat16: 1}
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need_cuda(name: str, *ts: Optional[torch.Tensor]) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name}: every tensor must be on the GPU")
+
+
+def mask(mode: int, W: int, B: int, G: int, causal: bool = True) -> DaMask:
+    return DaMask(int(mode), int(W), int(B), int(G), int(bool(causal)))
+
+
+def keep_count(m: DaMask, pos: int, prompt_len: int, n_keys: int = 0) -> int:
+    r = load().da_keep_count(m, pos, prompt_len, n_keys)
+    check(0 if r >= 0 else int(r), "da_keep_count")
+    return int(r)
+
+
+def keep_cap(m: DaMask, max_pos: int, max_prompt: int, n_keys: int = 0) -> int:
+    r = load().da_keep_cap(m, max_pos, max_prompt, n_keys)
+    check(0 if r >= 0 else int(r), "da_keep_cap")
+    return int(r)
+
+
+def keepset_build(m: DaMask, pos: torch.Tensor, prompt_len: torch.Tensor, cap: int,
+                  n_keys: int = 0, max_runs: int = 0, count=None, idx=None,
+                  n_runs=None, runs=None):
+    """Returns (count [n_q], idx [n_q, cap], n_runs [n_q] or None,
+    runs [n_q, max_runs, 2] or None), all int32 on pos.device."""
+    _need_cuda("keepset_build", pos, prompt_len)
+    n_q = pos.numel()
+    dev = pos.device
+    if count is None:
+        count = torch.empty(n_q, dtype=torch.int32, device=dev)
+    if idx is None:
+        idx = torch.empty((n_q, cap), dtype=torch.int32, device=dev)
+    if max_runs > 0:
+        if n_runs is None:
+            n_runs = torch.empty(n_q, dtype=torch.int32, device=dev)
+        if runs is None:
+            runs = torch.empty((n_q, max_runs, 2), dtype=torch.int32, device=dev)
+    for t in (pos, prompt_len, count, idx, n_runs, runs):
+        if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+            raise ValueError("keepset_build: int32 contiguous tensors expected")
+    check(load().da_keepset_build(m, n_q, _ptr(pos), _ptr(prompt_len), n_keys, cap,
+                                  _ptr(count), _ptr(idx), max_runs, _ptr(n_runs), _ptr(runs),
+                                  _stream(pos)),
+          "da_keepset_build")
+    return count, idx, n_runs, runs
+
+
+def kv_cache(k: torch.Tensor, v: torch.Tensor,
+             block_table: Optional[torch.Tensor] = None) -> DaKvCache:
+    """Descriptor for a contiguous [n_seq, hkv, Lmax, hd] cache (no block
+    table) or a paged [n_pages, hkv, page_size, hd] cache."""
+    if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("k and v caches must share shape, strides and dtype")
+    if k.dim() != 4 or k.stride(3) != 1:
+        raise ValueError("cache must be 4-D with a contiguous head_dim")
+    d = DaKvCache()
+    d.k, d.v = k.data_ptr(), v.data_ptr()
+    d.page_stride, d.head_stride, d.slot_stride = k.stride(0), k.stride(1), k.stride(2)
+    if block_table is not None:
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_contiguous():
+            raise ValueError("block_table must be a contiguous int32 [n_seq, pages] tensor")
+        d.page_size = k.shape[2]
+        d.bt_stride = block_table.shape[1]
+        d.block_table = block_table.data_ptr()
+    else:
+        d.page_size, d.bt_stride, d.block_table = 0, 0, None
+    return d
+
+
+def decode_workspace_bytes(n_q: int, hq: int, head_dim: int, cap: int, split: int) -> int:
+    r = load().da_decode_workspace_bytes(n_q, hq, head_dim, cap, split)
+    check(0 if r >= 0 else int(r), "da_decode_workspace_bytes")
+    return int(r)
+
+
+def sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                       seq: torch.Tensor, count: torch.Tensor, idx: torch.Tensor, *,
+                       split: int, block_table: Optional[torch.Tensor] = None,
+                       scale: Optional[float] = None, out=None, lse=None,
+                       want_lse: bool = False, workspace=None):
+    """q [n_q, hq, hd]; caches as in ``kv_cache``; seq/count [n_q] int32;
+    idx [n_q, cap] int32.  Returns (out [n_q, hq, hd], lse [n_q, hq] or None)."""
+    _need_cuda("sparse_decode_attn", q, k_cache, v_cache, seq, count, idx, block_table)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [n_q, hq, hd] tensor")
+    if q.dtype not in _DTYPE or q.dtype != k_cache.dtype:
+        raise ValueError("q and the caches must share dtype fp32 or bf16")
+    n_q, hq, hd = q.shape
+    hkv = k_cache.shape[1]
+    if idx.dim() != 2 or idx.shape[0] != n_q or not idx.is_contiguous():
+        raise ValueError("idx must be a contiguous [n_q, cap] tensor")
+    cap = idx.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(hd)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((n_q, hq), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(n_q, hq, hd, cap, split)
+    if need > 0 and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    kv = kv_cache(k_cache, v_cache, block_table)
+    check(load().da_sparse_decode_attn(_ptr(q), _DTYPE[q.dtype], n_q, hq, hkv, hd, float(scale),
+                                       kv, _ptr(seq), _ptr(count), _ptr(idx), cap, split,
+                                       _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                       _stream(q)),
+          "da_sparse_decode_attn")
+    return out, lse

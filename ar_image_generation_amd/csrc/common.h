@@ -1,0 +1,94 @@
+// Shared device and host helpers of libdiagattn (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/diagattn.h"
+
+namespace da {
+
+// ---------------------------------------------------------------- host side
+
+// Records `msg` as the calling thread's last error and returns `code`.
+int fail(int code, const char* fmt, ...);
+// Clears the thread's last error.
+void clear_error();
+// Checks hipGetLastError() after a launch; returns DA_OK or DA_EHIP.
+int check_launch(const char* what);
+// Validates a mask; DA_OK or DA_EINVAL with the reason recorded.
+int check_mask(const da_mask* m);
+
+inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+inline int ilog2(int64_t x) {
+  int r = 0;
+  while ((int64_t(1) << r) < x) ++r;
+  return r;
+}
+
+// Window-part keep test shared by the host count and the device builder:
+// d = i - j for a key j >= P inside the window range.  Future keys (d < 0,
+// matrix form only) are kept within B; past keys within B of the main
+// diagonal (BAND) or of any raster-row diagonal k*G (ROWDIAG).
+__host__ __device__ inline bool window_keep(int mode, int d, int B, int G) {
+  if (d < 0) return -d <= B;
+  if (mode == DA_MODE_BAND) return d <= B;
+  const int r = d % G;
+  return r <= B || G - r <= B;
+}
+
+// ---------------------------------------------------------------- device side
+
+// 16-byte vector of raw bits (8 bf16 or 4 fp32).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN -> quiet NaN).
+__device__ inline uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Unpacks one 16-byte chunk into EPL floats.
+template <int EPL>
+__device__ inline void unpack(const u32x4 w, float (&x)[EPL]) {
+  if constexpr (EPL == 8) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf16_lo(w[e]);
+      x[2 * e + 1] = bf16_hi(w[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
+  }
+}
+
+// DPP lane moves within 16-lane rows.
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+// Sum over aligned groups of N consecutive lanes (N = 8, 16 or 32); every
+// lane of the group receives the group sum.
+template <int N>
+__device__ inline float group_sum(float x) {
+  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  x += dpp<DPP_XOR1>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_HALF_MIRROR>(x);
+  if constexpr (N >= 16) x += dpp<DPP_MIRROR>(x);
+  if constexpr (N == 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+}  // namespace da

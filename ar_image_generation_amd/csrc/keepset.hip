@@ -1,0 +1,142 @@
+// keepset_build: per-query ascending KV index lists and maximal runs.
+//
+// One wave per query.  The prompt part [0, min(P, L)) is written directly;
+// the window part [max(P, i - W), i] (plus future keys within B in the matrix
+// form) is scanned 64 positions at a time: each lane tests one position with
+// window_keep(), a ballot gives the kept lanes and a popcount of the lanes
+// below gives each kept position its slot, so the list comes out ascending
+// with no sort and no atomics.  Run ends are found the same way; each end
+// lane walks back to its run's first position (runs inside the window are
+// at most a band wide, 2B + 1 positions, unless bands overlap).
+#include "common.h"
+
+namespace da {
+
+struct KeepsetArgs {
+  int mode, W, B, G, causal;
+  int n_q, n_keys, cap, max_runs;
+  const int32_t* pos;
+  const int32_t* prompt;
+  int32_t* count;
+  int32_t* idx;
+  int32_t* n_runs;
+  int32_t* runs;
+};
+
+__global__ void __launch_bounds__(256) keepset_kernel(KeepsetArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (q >= a.n_q) return;
+  const int i = a.pos[q];
+  const int P = a.prompt[q];
+  const bool bad = i < 0 || P < 0 || (!a.causal && i >= a.n_keys);
+  if (bad) {
+    if (lane == 0) {
+      a.count[q] = 0;
+      if (a.n_runs) a.n_runs[q] = 0;
+    }
+    return;
+  }
+  const int L = a.causal ? i + 1 : a.n_keys;
+  int32_t* my_idx = a.idx + (int64_t)q * a.cap;
+  int32_t* my_runs = a.runs ? a.runs + (int64_t)q * a.max_runs * 2 : nullptr;
+
+  int Pc, wlo, whi;
+  if (a.mode == DA_MODE_DENSE) {
+    Pc = L;           // everything up to L is one run
+    wlo = 1;
+    whi = 0;          // empty window
+  } else {
+    Pc = P < L ? P : L;
+    wlo = i - a.W > Pc ? i - a.W : Pc;
+    whi = a.causal ? i : (L - 1 < i + a.B ? L - 1 : i + a.B);
+  }
+
+  const int pw = Pc < a.cap ? Pc : a.cap;
+  for (int r = lane; r < pw; r += 64) my_idx[r] = r;
+
+  // The prompt run is run 0 unless the first window position continues it.
+  const bool joins = Pc > 0 && wlo == Pc && wlo <= whi &&
+                     window_keep(a.mode, i - wlo, a.B, a.G);
+  int nr = 0;
+  if (Pc > 0 && !joins) {
+    if (lane == 0 && my_runs && a.max_runs > 0) {
+      my_runs[0] = 0;
+      my_runs[1] = Pc;
+    }
+    nr = 1;
+  }
+
+  int n = Pc;
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int base = wlo; base <= whi; base += 64) {
+    const int j = base + lane;
+    const bool kp = j <= whi && window_keep(a.mode, i - j, a.B, a.G);
+    const uint64_t kb = __ballot(kp);
+    if (kp) {
+      const int slot = n + __popcll(kb & below);
+      if (slot < a.cap) my_idx[slot] = j;
+    }
+    n += __popcll(kb);
+
+    const bool next = j + 1 <= whi && window_keep(a.mode, i - j - 1, a.B, a.G);
+    const bool end = kp && !next;
+    const uint64_t eb = __ballot(end);
+    if (end && my_runs) {
+      const int k = nr + __popcll(eb & below);
+      int s = j;
+      while (s - 1 >= wlo && window_keep(a.mode, i - (s - 1), a.B, a.G)) --s;
+      if (s == wlo && joins) s = 0;
+      if (k < a.max_runs) {
+        my_runs[2 * k] = s;
+        my_runs[2 * k + 1] = j - s + 1;
+      }
+    }
+    nr += __popcll(eb);
+  }
+  if (lane == 0) {
+    a.count[q] = n;
+    if (a.n_runs) a.n_runs[q] = nr;
+  }
+}
+
+}  // namespace da
+
+using namespace da;
+
+extern "C" int da_keepset_build(const da_mask* m, int32_t n_q, const int32_t* pos,
+                                const int32_t* prompt_len, int32_t n_keys, int32_t cap,
+                                int32_t* count, int32_t* idx, int32_t max_runs,
+                                int32_t* n_runs, int32_t* runs, void* stream) {
+  int rc = check_mask(m);
+  if (rc) return rc;
+  if (n_q < 0) return fail(DA_EINVAL, "n_q=%d < 0", n_q);
+  if (n_q > 0 && (!pos || !prompt_len || !count || !idx))
+    return fail(DA_EINVAL, "pos, prompt_len, count and idx must be non-NULL");
+  if (cap < 1) return fail(DA_EINVAL, "cap=%d < 1", cap);
+  if (!m->causal && n_keys < 1) return fail(DA_EINVAL, "matrix form needs n_keys >= 1");
+  if ((runs == nullptr) != (n_runs == nullptr))
+    return fail(DA_EINVAL, "runs and n_runs must both be given or both be NULL");
+  if (runs && max_runs < 1) return fail(DA_EINVAL, "max_runs=%d < 1", max_runs);
+  clear_error();
+  if (n_q == 0) return DA_OK;
+  KeepsetArgs a;
+  a.mode = m->mode;
+  a.W = m->W;
+  a.B = m->B;
+  a.G = m->G;
+  a.causal = m->causal;
+  a.n_q = n_q;
+  a.n_keys = n_keys;
+  a.cap = cap;
+  a.max_runs = runs ? max_runs : 0;
+  a.pos = pos;
+  a.prompt = prompt_len;
+  a.count = count;
+  a.idx = idx;
+  a.n_runs = n_runs;
+  a.runs = runs;
+  const int blocks = (n_q + 3) / 4;
+  hipLaunchKernelGGL(keepset_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, a);
+  return check_launch("keepset_kernel");
+}

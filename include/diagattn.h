@@ -1,0 +1,179 @@
+/*
+ * diagattn.h -- C ABI of libdiagattn.so: diagonal-aware sparse attention for
+ * autoregressive image generation on MI355X (gfx950).
+ *
+ * The operation.  "Understanding and Exploiting Diagonal Attention Sparsity in
+ * Autoregressive Image Generation" (arXiv 2609.19702) computes, per query,
+ * softmax(Q K^T / sqrt(d) (.) M) V where M keeps key j for query i when
+ * |i - j| <= B and j >= i - W (paper-daily summary page, section
+ * "核心公式与算法", core formulas).  Masked keys are skipped: they are never
+ * read and get no weight (same summary, section "具体技术细节示例", the
+ * worked example, which normalises over the kept keys and counts only their
+ * KV reads).  The arXiv abstract names the two other facts used here:
+ * attention concentrates on the prompt tokens, and the diagonal pattern comes
+ * from the spatial locality of visual tokens in raster order.  Hence the
+ * keep-set of a decode query at position i with a prompt of P tokens is
+ *
+ *   DENSE   : every j <= i                                  (the baseline)
+ *   BAND    : j < P, or |i - j| <= B and j >= i - W          (the printed M)
+ *   ROWDIAG : j < P, or j >= i - W and |(i - j) - k*G| <= B for some k >= 0
+ *             (the main band plus one band per raster row above, G = grid
+ *             width; distances are plain sequence distances)
+ *
+ * with j <= i (causal) in decode.  Masked logits are -inf; the scale is
+ * 1/sqrt(head_dim) unless the caller passes another; query head h reads kv
+ * head h / (hq / hkv).
+ *
+ * Conventions.
+ *   - Every pointer is a DEVICE pointer owned by the caller unless marked
+ *     [host].  The library allocates no memory and keeps no state besides a
+ *     thread-local error string.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No call synchronises the device or copies host<->device.
+ *   - Host-checkable argument errors return a negative da_status before any
+ *     launch; da_last_error() then describes the problem.  A failed kernel
+ *     launch returns DA_EHIP with the HIP error text.  Values that live in
+ *     device memory (positions, counts, indices, block tables) cannot be
+ *     checked on the host: their preconditions are stated per call.
+ *   - Floating point: inputs and outputs share one dtype (fp32 or bf16);
+ *     accumulation and softmax state are fp32; bf16 outputs are rounded to
+ *     nearest even.
+ */
+#ifndef DIAGATTN_H
+#define DIAGATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DA_OK = 0,
+  DA_EINVAL = -1,     /* bad argument (null pointer, negative size, ...) */
+  DA_ENOTSUP = -2,    /* valid but unsupported (head_dim, dtype, group) */
+  DA_ECAPACITY = -3,  /* a caller-provided buffer is too small */
+  DA_EHIP = -4        /* a HIP runtime call or kernel launch failed */
+} da_status;
+
+typedef enum { DA_MODE_DENSE = 0, DA_MODE_BAND = 1, DA_MODE_ROWDIAG = 2 } da_mode;
+
+typedef enum { DA_F32 = 0, DA_BF16 = 1 } da_dtype;
+
+/* Mask parameters.  W and B are in tokens (a window of r raster rows is
+ * W = r * G).  causal = 1: a query at position i sees keys 0..i (decode and
+ * prefill); causal = 0: it sees keys 0..n_keys-1 (the N x N matrix form of
+ * the summary's mask, where future keys within B are kept too). */
+typedef struct {
+  int32_t mode;    /* da_mode */
+  int32_t W;       /* recent window, >= 0 */
+  int32_t B;       /* diagonal half-width, >= 0 */
+  int32_t G;       /* raster grid width, >= 1 (used by ROWDIAG) */
+  int32_t causal;  /* 0 or 1 */
+} da_mask;
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t da_version(void);
+
+/* Text of the last non-OK status returned on the calling thread ("" if none). */
+const char* da_last_error(void);
+
+/* [host] Exact keep-set size of one query at `pos` with `prompt_len` prompt
+ * tokens (n_keys is read only when m->causal == 0).  Returns a negative
+ * da_status for invalid arguments. */
+int64_t da_keep_count(const da_mask* m, int32_t pos, int32_t prompt_len, int32_t n_keys);
+
+/* [host] Upper bound on the keep-set size of any query with pos <= max_pos
+ * and prompt_len <= max_prompt (n_keys as above); use it to size `cap`. */
+int64_t da_keep_cap(const da_mask* m, int32_t max_pos, int32_t max_prompt, int32_t n_keys);
+
+/* keepset_build -- per-query KV index lists and their maximal runs.
+ *
+ * For each query q < n_q at position pos[q] with prompt_len[q] tokens of
+ * prompt, writes its keep-set (rule above) as ascending positions:
+ *   count[q]              number of kept keys (the true size, even if > cap)
+ *   idx[q*cap + r]        r-th kept position, for r < min(count[q], cap)
+ *   n_runs[q]             number of maximal runs of consecutive positions
+ *   runs[(q*max_runs + k)*2 + {0,1}] = (first position, length) of run k,
+ *                         for k < min(n_runs[q], max_runs)
+ * runs/n_runs may both be NULL (then max_runs is ignored).  Entries of idx
+ * and runs past count / n_runs are left untouched.
+ *
+ * Preconditions on device data: 0 <= pos[q]; 0 <= prompt_len[q]; for
+ * causal = 0 also pos[q] < n_keys.  Queries that break them get count 0.
+ * Overflow is reported, never written: if count[q] > cap (or n_runs[q] >
+ * max_runs) the caller's list for q is truncated and must be treated as an
+ * error (da_keep_cap gives a safe cap).
+ * Errors: DA_EINVAL for null required pointers, n_q < 0, cap < 1, W/B < 0,
+ * G < 1, mode or causal out of range, causal = 0 with n_keys < 1,
+ * runs/n_runs given with max_runs < 1 or only one of them given. */
+int da_keepset_build(const da_mask* m /* [host] */, int32_t n_q,
+                     const int32_t* pos, const int32_t* prompt_len, int32_t n_keys,
+                     int32_t cap, int32_t* count, int32_t* idx,
+                     int32_t max_runs, int32_t* n_runs, int32_t* runs,
+                     void* stream);
+
+/* KV cache descriptor: one form for contiguous and paged caches.
+ * Element (kv head g, logical position j) of request s starts at
+ *   base + page * page_stride + g * head_stride + slot * slot_stride
+ * with page = block_table[s * bt_stride + j / page_size] and
+ * slot = j % page_size; when block_table is NULL, page = s and slot = j
+ * (a contiguous [n_seq][hkv][Lmax][head_dim] cache has
+ * page_stride = hkv*Lmax*hd, head_stride = Lmax*hd, slot_stride = hd).
+ * Strides are in elements; head_dim elements of one row are contiguous and
+ * 16-byte aligned.  page_size must be a power of two when block_table is set. */
+typedef struct {
+  const void* k;
+  const void* v;
+  int64_t page_stride;
+  int64_t head_stride;
+  int64_t slot_stride;
+  int32_t page_size;
+  int32_t bt_stride;
+  const int32_t* block_table;   /* [n_seq][bt_stride] or NULL */
+} da_kv_cache;
+
+/* [host] Workspace bytes da_sparse_decode_attn needs for these sizes (0 when
+ * every keep-set fits one split, i.e. cap <= split). */
+int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t head_dim,
+                                  int32_t cap, int32_t split);
+
+/* sparse_decode_attn -- one decode step of masked attention over kept keys.
+ *
+ * out[q][h][:] = sum_r w_r V[g, idx[q*cap + r]] with
+ * w = softmax_r(scale * q[q][h] . K[g, idx[q*cap + r]]), r < count[q],
+ * g = h / (hq/hkv), K/V rows of request seq[q] read through `kv`.
+ * This is the summary's masked softmax with the exclusion reading: only the
+ * count[q] listed keys are loaded and weighted (worked example).  A DENSE
+ * keep-set (every j <= pos) makes this the dense baseline at the same shape.
+ *
+ * Work split: each query's list is cut into chunks of `split` keys; each
+ * (query, kv head, chunk) is one workgroup that serves all hq/hkv query heads
+ * of the kv head, so each kept K/V row is read from HBM once.  Chunks are
+ * combined by a log-sum-exp merge (a second kernel, only when cap > split).
+ *
+ *   q     [n_q][hq][head_dim] in `dtype`
+ *   out   [n_q][hq][head_dim] in `dtype`
+ *   lse   [n_q][hq] fp32 natural-log sum of exp of the scaled logits, or NULL
+ *   seq   [n_q] request (block-table row) of each query
+ *   count [n_q], idx [n_q][cap] as written by da_keepset_build
+ *   workspace: da_decode_workspace_bytes(...) bytes, 256-byte aligned, or NULL
+ *         when that is 0; its contents need no initialisation.
+ * Preconditions on device data: 1 <= count[q] (counts above cap are read as
+ * cap); every listed position addresses a valid cache row of request seq[q].
+ * Errors: DA_EINVAL (null pointers, n_q < 0, hq or hkv < 1, hq % hkv != 0,
+ * cap < 1, split < 1, non-power-of-two page_size with a block table,
+ * bt_stride < 1), DA_ENOTSUP (head_dim not 64/128, dtype, hq/hkv not in
+ * {1,2,4,8}, split > 256), DA_ECAPACITY (workspace too small). */
+int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
+                          int32_t hq, int32_t hkv, int32_t head_dim, float scale,
+                          const da_kv_cache* kv /* [host] */, const int32_t* seq,
+                          const int32_t* count, const int32_t* idx, int32_t cap,
+                          int32_t split, void* out, float* lse,
+                          void* workspace, int64_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIAGATTN_H */

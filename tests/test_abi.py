@@ -1,0 +1,115 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+and its host-side paths (sizing, argument checks) behave as documented.
+No kernel is launched here."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ar_image_generation_amd as da
+from ar_image_generation_amd import _native
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*[A-Za-z_][\w\s\*]*?\b(da_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = da.load()
+    names = declared_symbols()
+    assert {"da_keepset_build", "da_sparse_decode_attn", "da_keep_count"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _native.SIGNATURES, n
+
+
+def test_version_and_error_text():
+    assert da.load().da_version() >= 100
+    with pytest.raises(da.DiagAttnError, match="mode 7"):
+        da.keep_count(da.mask(7, 1, 1, 1), 0, 0)
+
+
+@pytest.mark.parametrize("mode", [O.DENSE, O.BAND, O.ROWDIAG])
+def test_keep_count_matches_oracle(mode):
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        P, W, B, G = (int(rng.integers(0, 40)), int(rng.integers(0, 70)),
+                      int(rng.integers(0, 6)), int(rng.integers(1, 20)))
+        causal = bool(rng.integers(0, 2))
+        n_keys = int(rng.integers(1, 200))
+        i = int(rng.integers(0, n_keys if not causal else 300))
+        m = da.mask(mode, W, B, G, causal)
+        want = len(O.keepset(i, n_keys if not causal else None, P=P, W=W, B=B, G=G,
+                             mode=mode, causal=causal))
+        assert da.keep_count(m, i, P, n_keys) == want, (mode, P, W, B, G, causal, i, n_keys)
+        assert da.keep_cap(m, i, P, n_keys) >= want
+
+
+def test_keep_cap_bounds_the_workloads():
+    for (P, W, B, G, mode, maxpos) in [(16, 64, 2, 16, O.ROWDIAG, 271), (120, 96, 2, 32, O.ROWDIAG, 1143),
+                                       (300, 96, 2, 48, O.BAND, 2603), (256, 256, 3, 64, O.DENSE, 4351)]:
+        m = da.mask(mode, W, B, G)
+        cap = da.keep_cap(m, maxpos, P)
+        for i in range(0, maxpos + 1, 7):
+            assert da.keep_count(m, i, P) <= cap
+
+
+def test_argument_errors_are_reported_before_launch():
+    lib = da.load()
+    m = da.mask(O.ROWDIAG, 4, 1, 3)
+    dummy = ctypes.c_void_p(16)   # never dereferenced: checks fail first
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 0, dummy, dummy, 0, None, None, None)
+    assert rc == -1 and "cap" in _native.last_error()
+    rc = lib.da_keepset_build(m, -1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, None)
+    assert rc == -1
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 2, None, dummy, None)
+    assert rc == -1 and "both" in _native.last_error()
+    bad = da.mask(O.BAND, -1, 1, 3)
+    assert lib.da_keepset_build(bad, 1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, None) == -1
+    nc = da.mask(O.BAND, 1, 1, 3, causal=False)
+    assert lib.da_keepset_build(nc, 1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, None) == -1
+    # zero queries is a valid no-op
+    assert lib.da_keepset_build(m, 0, None, None, 0, 4, None, None, 0, None, None, None) == 0
+
+    kv = _native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None)
+
+    def dec(dtype=1, n_q=1, hq=8, hkv=2, hd=128, cap=64, split=64, ws=None, wsb=0, kvd=kv, q=dummy):
+        return lib.da_sparse_decode_attn(q, dtype, n_q, hq, hkv, hd, 0.1, kvd, dummy, dummy,
+                                         dummy, cap, split, dummy, None, ws, wsb, None)
+    assert dec(hq=6, hkv=4) == -1
+    assert dec(hd=96) == -2
+    assert dec(dtype=3) == -2
+    assert dec(hq=48, hkv=3) == -2          # group 16
+    assert dec(split=0) == -1
+    assert dec(split=300) == -2
+    assert dec(cap=200, split=64) == -3     # needs a workspace
+    assert "workspace" in _native.last_error()
+    paged = _native.DaKvCache(16, 16, 0, 0, 0, 12, 4, 16)
+    assert dec(kvd=paged) == -1 and "power of two" in _native.last_error()
+    assert dec(q=ctypes.c_void_p(8)) == -1   # misaligned q
+
+
+def test_decode_workspace_size():
+    assert da.decode_workspace_bytes(4, 8, 128, 64, 64) == 0
+    b = da.decode_workspace_bytes(4, 8, 128, 200, 64)
+    rows = 4 * 8 * 4
+    assert b >= rows * (128 + 2) * 4
+
+
+def test_product_path_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(_native, "_lib", None)
+    monkeypatch.setattr(_native, "LIB_PATH", "/nonexistent/libdiagattn.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _native.load()

@@ -14,5 +14,6 @@ from .generate import (  # noqa: F401
     PrefillInputs,
     correlated_field,
     decode_inputs,
+    positions,
     prefill_inputs,
 )

@@ -34,6 +34,7 @@ class DecodeConfig:
     kv_gen: str = "normal"  # "normal" | "field"
     seed: int = 0
     queries_per_seq: int = 1
+    split: int = 64         # listed keys per decode workgroup (launch setting)
 
     @property
     def n_vis(self) -> int:

@@ -108,6 +108,16 @@ def _positions(cfg: DecodeConfig, seed: int):
             seq.astype(np.int64))
 
 
+def positions(cfg: DecodeConfig, seed: Optional[int] = None):
+    """(pos, prompt_len, seq) int32 tensors of a decode workload, without
+    generating its cache."""
+    seed = cfg.seed if seed is None else seed
+    prompt_s, pos, seq = _positions(cfg, seed)
+    return (torch.from_numpy(pos.astype(np.int32)),
+            torch.from_numpy(prompt_s[seq].astype(np.int32)),
+            torch.from_numpy(seq.astype(np.int32)))
+
+
 def _fill_sequence(cfg: DecodeConfig, seed: int, s: int, P: int, lmax: int,
                    which: int) -> np.ndarray:
     """Logical K (which=0) or V (which=1) rows of request s, float32
