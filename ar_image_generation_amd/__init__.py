@@ -7,7 +7,9 @@ from .api import (  # noqa: F401
     BAND,
     DENSE,
     ROWDIAG,
+    decode_workspace,
     decode_workspace_bytes,
+    hbm_read_probe,
     keep_cap,
     keep_count,
     keepset_build,

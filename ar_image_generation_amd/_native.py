@@ -22,7 +22,7 @@ class DaMask(ctypes.Structure):
 class DaKvCache(ctypes.Structure):
     _fields_ = [("k", c_vp), ("v", c_vp), ("page_stride", c_i64), ("head_stride", c_i64),
                 ("slot_stride", c_i64), ("page_size", c_i32), ("bt_stride", c_i32),
-                ("block_table", c_vp)]
+                ("block_table", c_vp), ("n_seq", c_i32), ("n_pages", c_i32), ("max_len", c_i32)]
 
 
 # name -> (restype, argtypes); every symbol include/diagattn.h declares
@@ -34,6 +34,7 @@ SIGNATURES = {
     "da_keepset_build": (ctypes.c_int, [ctypes.POINTER(DaMask), c_i32, c_vp, c_vp, c_i32, c_i32,
                                         c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "da_decode_workspace_bytes": (c_i64, [c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "da_hbm_read_probe": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i32, c_vp]),
     "da_sparse_decode_attn": (ctypes.c_int, [c_vp, ctypes.c_int, c_i32, c_i32, c_i32, c_i32, c_f32,
                                              ctypes.POINTER(DaKvCache), c_vp, c_vp, c_vp, c_i32,
                                              c_i32, c_vp, c_vp, c_vp, c_i64, c_vp]),

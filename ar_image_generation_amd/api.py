@@ -79,7 +79,8 @@ def keepset_build(m: DaMask, pos: torch.Tensor, prompt_len: torch.Tensor, cap: i
 def kv_cache(k: torch.Tensor, v: torch.Tensor,
              block_table: Optional[torch.Tensor] = None) -> DaKvCache:
     """Descriptor for a contiguous [n_seq, hkv, Lmax, hd] cache (no block
-    table) or a paged [n_pages, hkv, page_size, hd] cache."""
+    table) or a paged [n_pages, hkv, page_size, hd] cache with a
+    [n_seq, pages_per_seq] int32 block table."""
     if k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
         raise ValueError("k and v caches must share shape, strides and dtype")
     if k.dim() != 4 or k.stride(3) != 1:
@@ -93,8 +94,13 @@ def kv_cache(k: torch.Tensor, v: torch.Tensor,
         d.page_size = k.shape[2]
         d.bt_stride = block_table.shape[1]
         d.block_table = block_table.data_ptr()
+        d.n_seq = block_table.shape[0]
+        d.n_pages = k.shape[0]
+        d.max_len = block_table.shape[1] * k.shape[2]
     else:
         d.page_size, d.bt_stride, d.block_table = 0, 0, None
+        d.n_seq = d.n_pages = k.shape[0]
+        d.max_len = k.shape[2]
     return d
 
 
@@ -104,13 +110,24 @@ def decode_workspace_bytes(n_q: int, hq: int, head_dim: int, cap: int, split: in
     return int(r)
 
 
+def decode_workspace(n_q: int, hq: int, head_dim: int, cap: int, split: int,
+                     device) -> Optional[torch.Tensor]:
+    """A decode workspace of the right size (None when none is needed)."""
+    need = decode_workspace_bytes(n_q, hq, head_dim, cap, split)
+    if need == 0:
+        return None
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
 def sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                        seq: torch.Tensor, count: torch.Tensor, idx: torch.Tensor, *,
                        split: int, block_table: Optional[torch.Tensor] = None,
                        scale: Optional[float] = None, out=None, lse=None,
                        want_lse: bool = False, workspace=None):
     """q [n_q, hq, hd]; caches as in ``kv_cache``; seq/count [n_q] int32;
-    idx [n_q, cap] int32.  Returns (out [n_q, hq, hd], lse [n_q, hq] or None)."""
+    idx [n_q, cap] int32.  ``workspace``: from ``decode_workspace`` (reusable
+    across calls on one stream); allocated per call when omitted.
+    Returns (out [n_q, hq, hd], lse [n_q, hq] or None)."""
     _need_cuda("sparse_decode_attn", q, k_cache, v_cache, seq, count, idx, block_table)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [n_q, hq, hd] tensor")
@@ -127,9 +144,8 @@ def sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
         out = torch.empty_like(q)
     if want_lse and lse is None:
         lse = torch.empty((n_q, hq), dtype=torch.float32, device=q.device)
-    need = decode_workspace_bytes(n_q, hq, hd, cap, split)
-    if need > 0 and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(n_q, hq, hd, cap, split, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     kv = kv_cache(k_cache, v_cache, block_table)
     check(load().da_sparse_decode_attn(_ptr(q), _DTYPE[q.dtype], n_q, hq, hkv, hd, float(scale),
@@ -138,3 +154,16 @@ def sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                                        _stream(q)),
           "da_sparse_decode_attn")
     return out, lse
+
+
+def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int,
+                   nbytes: Optional[int] = None, offset: int = 0) -> None:
+    """Streams `nbytes` bytes of `buf` starting at byte `offset` (measurement)."""
+    _need_cuda("hbm_read_probe", buf, sink)
+    total = buf.numel() * buf.element_size()
+    nbytes = total - offset if nbytes is None else nbytes
+    if offset < 0 or offset + nbytes > total or sink.numel() < grid or sink.element_size() != 4:
+        raise ValueError("hbm_read_probe: range outside the buffer or sink too small")
+    check(load().da_hbm_read_probe(buf.data_ptr() + offset, nbytes, sink.data_ptr(), grid,
+                                   _stream(buf)),
+          "da_hbm_read_probe")

@@ -2,20 +2,28 @@
 //
 // Grid: one 256-thread workgroup per (query, kv head, chunk of `split`
 // listed keys).  Each K/V row (head_dim elements, 128-512 bytes) is read by
-// LPR = row_bytes / 16 consecutive lanes with one 16-byte load each, so a
-// wave instruction moves 64 x 16 = 1 KiB and rows of a run are contiguous
-// in memory.  A thread owns NP row slots of the chunk and issues all of its
-// K and V loads before any arithmetic, so the whole chunk (up to 128 KiB per
-// workgroup) is in flight at once: the kernel is bound by HBM bandwidth on
-// the kept bytes and has no other use for the data, so it is not staged
-// through LDS; LDS only carries the cross-wave softmax/output reduction.
+// LPR = row_bytes / 16 consecutive lanes with one 16-byte load each, so one
+// wave instruction moves 1 KiB and the rows of a run are contiguous in
+// memory.  A thread owns NP row slots of the chunk.  Loads are issued in
+// three phases -- every index, then (paged caches) every block-table entry,
+// then every K and V row -- so a workgroup's whole chunk (up to 128 KiB) is
+// in flight after two short dependent latencies.  The kernel is bound by HBM
+// bandwidth on the kept bytes and uses each byte once, so K/V go straight to
+// registers; LDS only carries the cross-wave softmax/output reduction.
 //
 // All hq/hkv query heads that share a kv head are served by the same
 // workgroup, so each kept row is read once.  Scores are q . k scaled by
-// log2(e)/sqrt(d) (folded into q) and reduced across a row's lanes with DPP;
+// log2(e)/sqrt(d) (folded into q) and summed across a row's lanes with DPP;
 // the chunk's max, sum and sum p*v follow.  A query whose list fits one
-// chunk writes its normalised output directly; otherwise chunks leave
-// (max, sum, unnormalised o) partials and merge_kernel combines them.
+// chunk writes its normalised output directly.  Otherwise each chunk stores
+// a (max, sum, unnormalised o) partial and merge_kernel combines them by
+// log-sum-exp.  (Merging inside the decode kernel by the last-arriving chunk
+// needs agent-scope fences, which write back and invalidate the whole L2 of
+// the XCD on this part: measured far slower than a second launch.)
+//
+// Every index read from device memory (request, position, page) is clamped
+// into the cache extents the host passes, so no list content can make the
+// kernel read outside the cache.
 #include "common.h"
 
 namespace da {
@@ -30,6 +38,7 @@ struct DecodeArgs {
   int64_t page_stride, head_stride, slot_stride;
   const int32_t* block_table;
   int bt_stride, ps_shift, ps_mask;
+  int n_seq, n_pages, max_len;      // extents for clamping
   const int32_t* seq;
   const int32_t* count;
   const int32_t* idx;
@@ -41,8 +50,27 @@ struct DecodeArgs {
   float* ws_ml;           // [n_q][hq][max_split][2]
 };
 
-template <bool BF16>
-__device__ inline void store_chunk(void* base, int64_t off, const float* x, int epl) {
+// Workspace layout: partial outputs, then partial (max, sum) pairs.
+struct WsLayout {
+  int64_t o_off, ml_off, bytes;
+};
+
+static inline int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+static WsLayout ws_layout(int64_t n_q, int64_t hq, int64_t hd, int64_t ns) {
+  WsLayout w{0, 0, 0};
+  if (ns <= 1) return w;
+  const int64_t rows = n_q * hq * ns;
+  w.o_off = 0;
+  w.ml_off = align256(rows * hd * 4);
+  w.bytes = w.ml_off + align256(rows * 2 * 4);
+  return w;
+}
+
+__device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+template <bool BF16, int EPL>
+__device__ inline void store_out(void* base, int64_t off, const float* x) {
   if constexpr (BF16) {
     uint32_t w[4];
 #pragma unroll
@@ -55,15 +83,70 @@ __device__ inline void store_chunk(void* base, int64_t off, const float* x, int 
   }
 }
 
-template <bool BF16, int HD, int GRP, int TMAX>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
-  constexpr int ES = BF16 ? 2 : 4;
-  constexpr int EPL = 16 / ES;            // elements per 16-byte chunk
-  constexpr int LPR = HD * ES / 16;       // lanes per row
-  constexpr int RPP = 256 / LPR;          // rows per pass of the workgroup
-  constexpr int NP = (TMAX + RPP - 1) / RPP;
-  constexpr int WROWS = 64 / LPR;         // row slots per wave per pass
+// One tile = NP passes of the workgroup = NP * (256 / LPR) listed rows.
+template <bool BF16, int HD, int NP>
+struct Tile {
+  static constexpr int ES = BF16 ? 2 : 4;
+  static constexpr int EPL = 16 / ES;
+  static constexpr int LPR = HD * ES / 16;
+  static constexpr int RPP = 256 / LPR;
+  static constexpr int ROWS = NP * RPP;
+  u32x4 k[NP], v[NP];
 
+  // Issues the K and V loads of tile t (no waits).  Slots past the chunk
+  // read position 0's row (always valid, and shared, so it costs cache hits).
+  __device__ inline void load(const char* kb, const char* vb, const int64_t* off, int64_t off0,
+                              int t, int rsub, int nrows) {
+    int64_t o[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int r = t * ROWS + p * RPP + rsub;
+      o[p] = off[r < nrows ? r : nrows - 1];
+      o[p] = r < nrows ? o[p] : off0;
+    }
+    // all LDS reads first, then all global loads: one LDS wait per tile
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      k[p] = *reinterpret_cast<const u32x4*>(kb + o[p] * ES);
+      v[p] = *reinterpret_cast<const u32x4*>(vb + o[p] * ES);
+    }
+  }
+};
+
+// q . k over this lane's 16-byte chunk: bf16 pairs through v_dot2, fp32 by FMA.
+template <bool BF16>
+__device__ inline float chunk_dot(const u32x4 q, const u32x4 k, const float* qf) {
+  if constexpr (BF16) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // copy to scalars first: bit-casting a vector element directly makes
+      // this compiler read element 0 for every e
+      const uint32_t qe = q[e], ke = k[e];
+      d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qe),
+                                          __builtin_bit_cast(bf16x2, ke), d, false);
+    }
+    return d;
+  } else {
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) d = fmaf(qf[e], __uint_as_float(k[e]), d);
+    return d;
+  }
+}
+
+template <bool BF16, int HD, int GRP, int NP>
+__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+  using TL = Tile<BF16, HD, NP>;
+  constexpr int ES = TL::ES;
+  constexpr int EPL = TL::EPL;
+  constexpr int LPR = TL::LPR;
+  constexpr int RPP = TL::RPP;
+  constexpr int ROWS = TL::ROWS;
+
+  extern __shared__ int64_t rowoff[];     // [split] element offset of each listed row
   __shared__ float red_m[4][GRP];
   __shared__ float red_l[4][GRP];
   __shared__ float red_o[4][GRP][HD];
@@ -78,165 +161,211 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int qg = bid / a.max_split;
   const int qi = qg / a.hkv;
   const int g = qg % a.hkv;
-
-  int cnt = a.count[qi];
-  cnt = cnt < a.cap ? cnt : a.cap;
   const int r0 = s * a.split;
-  if (r0 >= cnt) return;
-  const int nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
-  const int sq = a.seq[qi];
-
-  const char* kb = reinterpret_cast<const char*>(a.k);
-  const char* vb = reinterpret_cast<const char*>(a.v);
   const int32_t* myidx = a.idx + (int64_t)qi * a.cap + r0;
+  const int lim = a.cap - r0 < a.split ? a.cap - r0 : a.split;   // >= 1
 
-  // ---- issue every K and V load of this thread's row slots
-  u32x4 kr[NP], vr[NP];
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int r = p * RPP + rsub;
-    if (r < nrows) {
-      const int j = myidx[r];
-      int64_t page, slot;
-      if (a.block_table) {
-        page = a.block_table[(int64_t)sq * a.bt_stride + (j >> a.ps_shift)];
-        slot = j & a.ps_mask;
-      } else {
-        page = sq;
-        slot = j;
-      }
-      const int64_t off = (page * a.page_stride + g * a.head_stride + slot * a.slot_stride + c * EPL) * ES;
-      kr[p] = *reinterpret_cast<const u32x4*>(kb + off);
-      vr[p] = *reinterpret_cast<const u32x4*>(vb + off);
-    } else {
-      kr[p] = u32x4{0, 0, 0, 0};
-      vr[p] = u32x4{0, 0, 0, 0};
-    }
-  }
-
-  // ---- this lane's slice of the GRP query heads, pre-scaled
-  float qf[GRP][EPL];
+  // ---- stage 0: query slices, list entries, count and request in one
+  // round trip (every load unconditional and in bounds)
+  u32x4 qw[GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
     const int64_t qoff = ((int64_t)qi * a.hq + g * GRP + h) * HD + c * EPL;
-    const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.q) + qoff * ES);
-    unpack<EPL>(w, qf[h]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[h][e] *= a.qscale;
+    qw[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.q) + qoff * ES);
   }
+  constexpr int IPT = 4;                  // list entries per thread per round
+  int jj[IPT];
+#pragma unroll
+  for (int u = 0; u < IPT; ++u) {
+    const int r = u * 256 + t;
+    jj[u] = myidx[r < lim ? r : lim - 1];
+  }
+  int cnt = a.count[qi];
+  const int sq_raw = a.seq[qi];
+  // compiler-only barrier: keeps the loads above ahead of the count test
+  // (they would otherwise be sunk behind it); emits nothing
+  __asm__ volatile("" ::: "memory");
+  cnt = cnt < a.cap ? cnt : a.cap;
+  if (r0 >= cnt) return;
+  const int nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
+  const int sq = clampi(sq_raw, 0, a.n_seq - 1);
 
-  // ---- scores (log2 domain)
-  float sc[NP][GRP];
+  // ---- stage 1: element offset of every listed row into LDS
+  const int32_t* bt = a.block_table ? a.block_table + (int64_t)sq * a.bt_stride : nullptr;
+  const int64_t off0 = bt ? (int64_t)clampi(bt[0], 0, a.n_pages - 1) * a.page_stride
+                          : (int64_t)sq * a.page_stride;
+  for (int base = 0; base < nrows; base += IPT * 256) {
+    if (base > 0) {
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    float kx[EPL];
-    unpack<EPL>(kr[p], kx);
+      for (int u = 0; u < IPT; ++u) {
+        const int r = base + u * 256 + t;
+        jj[u] = myidx[r < lim ? r : lim - 1];
+      }
+    }
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      float d = 0.f;
+    for (int u = 0; u < IPT; ++u) jj[u] = clampi(jj[u], 0, a.max_len - 1);
+    int64_t o[IPT];
+    if (bt) {
+      int pg[IPT];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) d = fmaf(qf[h][e], kx[e], d);
-      d = group_sum<LPR>(d);
-      sc[p][h] = (p * RPP + rsub < nrows) ? d : -INFINITY;
+      for (int u = 0; u < IPT; ++u) pg[u] = bt[jj[u] >> a.ps_shift];
+#pragma unroll
+      for (int u = 0; u < IPT; ++u)
+        o[u] = (int64_t)clampi(pg[u], 0, a.n_pages - 1) * a.page_stride +
+               (int64_t)(jj[u] & a.ps_mask) * a.slot_stride;
+    } else {
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) o[u] = (int64_t)sq * a.page_stride + (int64_t)jj[u] * a.slot_stride;
+    }
+#pragma unroll
+    for (int u = 0; u < IPT; ++u) {
+      const int r = base + u * 256 + t;
+      if (r < nrows) rowoff[r] = o[u];
     }
   }
-
-  // ---- chunk max per head
-  float mx[GRP];
-#pragma unroll
-  for (int h = 0; h < GRP; ++h) {
-    float m = sc[0][h];
-#pragma unroll
-    for (int p = 1; p < NP; ++p) m = fmaxf(m, sc[p][h]);
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-    mx[h] = m;
-  }
-  if ((t & 63) == 0) {
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) red_m[wave][h] = mx[h];
-  }
   __syncthreads();
+
+  // ---- query slices as fp32 (the fp32 path; bf16 uses the packed words)
+  float qf[GRP][4];
 #pragma unroll
   for (int h = 0; h < GRP; ++h)
-    mx[h] = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qf[h][e] = __uint_as_float(qw[h][e]) * a.qscale;
+  const float sscale = BF16 ? a.qscale : 1.f;
 
-  // ---- weights, their sum and sum p * v
-  float ls[GRP];
-  float acc[GRP][EPL];
+  // ---- stage 2: tiles of ROWS rows, two in flight; per-thread online softmax
+  const char* kb = reinterpret_cast<const char*>(a.k) + ((int64_t)g * a.head_stride + c * EPL) * ES;
+  const char* vb = reinterpret_cast<const char*>(a.v) + ((int64_t)g * a.head_stride + c * EPL) * ES;
+  float m[GRP], l[GRP], acc[GRP][EPL];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
-    ls[h] = 0.f;
+    m[h] = -INFINITY;
+    l[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
+  const int nt = (nrows + ROWS - 1) / ROWS;
+
+  auto process = [&](const TL& buf, int tt) {
+    float sc[NP][GRP];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    float vx[EPL];
-    unpack<EPL>(vr[p], vx);
+    for (int p = 0; p < NP; ++p) {
+      const bool valid = tt * ROWS + p * RPP + rsub < nrows;
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      const float w = exp2f(sc[p][h] - mx[h]);   // 0 for empty slots
-      ls[h] += w;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(w, vx[e], acc[h][e]);
+      for (int h = 0; h < GRP; ++h) {
+        const float d = group_sum<LPR>(chunk_dot<BF16>(qw[h], buf.k[p], qf[h])) * sscale;
+        sc[p][h] = valid ? d : -INFINITY;
+      }
     }
-  }
-  // reduce over the row slots of the wave (lanes with the same chunk c)
-#pragma unroll
-  for (int o = LPR; o < 64; o <<= 1) {
+    float mref[GRP];
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
-      ls[h] += __shfl_xor(ls[h], o);
+      float mt = sc[0][h];
+#pragma unroll
+      for (int p = 1; p < NP; ++p) mt = fmaxf(mt, sc[p][h]);
+      const float mn = fmaxf(m[h], mt);
+      mref[h] = mn == -INFINITY ? 0.f : mn;     // no valid row seen yet
+      const float f = exp2f(m[h] - mref[h]);
+      l[h] *= f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+      m[h] = mn;
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      float vx[EPL];
+      unpack<EPL>(buf.v[p], vx);
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        const float w = exp2f(sc[p][h] - mref[h]);
+        l[h] += w;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(w, vx[e], acc[h][e]);
+      }
+    }
+  };
+
+  TL b0, b1;
+  b0.load(kb, vb, rowoff, off0, 0, rsub, nrows);
+  for (int tt = 0; tt < nt; tt += 2) {
+    b1.load(kb, vb, rowoff, off0, tt + 1, rsub, nrows);
+    process(b0, tt);
+    if (tt + 1 >= nt) break;
+    b0.load(kb, vb, rowoff, off0, tt + 2, rsub, nrows);
+    process(b1, tt + 1);
+  }
+
+  // ---- combine the row slots of each wave (lanes with the same chunk c)
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) {
+    float M = m[h];
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float f = exp2f(m[h] - (M == -INFINITY ? 0.f : M));
+    l[h] *= f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] *= f;
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) {
+      l[h] += __shfl_xor(l[h], o);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[h][e] += __shfl_xor(acc[h][e], o);
     }
+    m[h] = M;
   }
-  // lanes 0..LPR-1 of each wave now hold the wave's totals
   if ((t & 63) < LPR) {
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) red_o[wave][h][c * EPL + e] = acc[h][e];
-      if (c == 0) red_l[wave][h] = ls[h];
+      if (c == 0) {
+        red_m[wave][h] = m[h];
+        red_l[wave][h] = l[h];
+      }
     }
   }
   __syncthreads();
 
-  // ---- combine the four waves; one thread per (head, chunk)
-  const bool single = cnt <= a.split;
+  // ---- combine the four waves; one thread per (head, 16-byte chunk)
   if (t < GRP * LPR) {
     const int h = t / LPR;
     const int cc = t % LPR;
+    float M = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+    float fw[4];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      fw[w] = exp2f(red_m[w][h] - M);          // M is finite: the chunk has rows
+      L = fmaf(fw[w], red_l[w][h], L);
+    }
     float o[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
-      o[e] = red_o[0][h][cc * EPL + e] + red_o[1][h][cc * EPL + e] +
-             red_o[2][h][cc * EPL + e] + red_o[3][h][cc * EPL + e];
-    const float l = red_l[0][h] + red_l[1][h] + red_l[2][h] + red_l[3][h];
-    const int head = g * GRP + h;
-    const int64_t row = (int64_t)qi * a.hq + head;
-    if (single) {
-      const float inv = 1.f / l;
+      o[e] = fw[0] * red_o[0][h][cc * EPL + e] + fw[1] * red_o[1][h][cc * EPL + e] +
+             fw[2] * red_o[2][h][cc * EPL + e] + fw[3] * red_o[3][h][cc * EPL + e];
+    const int64_t row = (int64_t)qi * a.hq + g * GRP + h;
+    if (cnt <= a.split) {
+      const float inv = 1.f / L;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] *= inv;
-      store_chunk<BF16>(a.out, row * HD + cc * EPL, o, EPL);
-      if (a.lse && cc == 0) a.lse[row] = (mx[h] + log2f(l)) * kLn2;
+      store_out<BF16, EPL>(a.out, row * HD + cc * EPL, o);
+      if (a.lse && cc == 0) a.lse[row] = (M + log2f(L)) * kLn2;
     } else {
       float* dst = a.ws_o + (row * a.max_split + s) * HD + cc * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; e += 4)
         *reinterpret_cast<float4*>(dst + e) = make_float4(o[e], o[e + 1], o[e + 2], o[e + 3]);
       if (cc == 0) {
-        a.ws_ml[(row * a.max_split + s) * 2] = mx[h];
-        a.ws_ml[(row * a.max_split + s) * 2 + 1] = l;
+        a.ws_ml[(row * a.max_split + s) * 2] = M;
+        a.ws_ml[(row * a.max_split + s) * 2 + 1] = L;
       }
     }
   }
 }
 
-// Log-sum-exp merge of a query head's chunk partials: one wave per
-// (query, head); only queries whose list spans more than one chunk.
+// Log-sum-exp merge of the chunk partials of one (query, head): one wave.
+// Lanes first read the chunks' (max, sum) pairs in parallel, then every lane
+// accumulates its HD/64 output elements over the chunks.
 template <bool BF16, int HD>
 __global__ void __launch_bounds__(64) merge_kernel(DecodeArgs a) {
   constexpr int EPT = HD / 64;
@@ -249,16 +378,22 @@ __global__ void __launch_bounds__(64) merge_kernel(DecodeArgs a) {
   const int ns = (cnt + a.split - 1) / a.split;
   const float* ml = a.ws_ml + (int64_t)row * a.max_split * 2;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, o[EPT];
+  for (int k = lane; k < ns; k += 64) M = fmaxf(M, ml[2 * k]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  float L = 0.f;
+  for (int k = lane; k < ns; k += 64) L += exp2f(ml[2 * k] - M) * ml[2 * k + 1];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+  float o[EPT];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) o[e] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = exp2f(ml[2 * s] - M);
-    L = fmaf(w, ml[2 * s + 1], L);
-    const float* src = a.ws_o + ((int64_t)row * a.max_split + s) * HD;
+  const float* src = a.ws_o + (int64_t)row * a.max_split * HD + lane * EPT;
+#pragma unroll 4
+  for (int k = 0; k < ns; ++k) {
+    const float w = exp2f(ml[2 * k] - M);
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) o[e] = fmaf(w, src[lane * EPT + e], o[e]);
+    for (int e = 0; e < EPT; ++e) o[e] = fmaf(w, src[(int64_t)k * HD + e], o[e]);
   }
   const float inv = 1.f / L;
   if constexpr (BF16) {
@@ -276,23 +411,26 @@ __global__ void __launch_bounds__(64) merge_kernel(DecodeArgs a) {
 typedef void (*decode_fn)(DecodeArgs);
 typedef void (*merge_fn)(DecodeArgs);
 
+// Tile depth: NP passes per tile (two tiles in flight per workgroup).
 template <bool BF16, int HD, int GRP>
-static decode_fn pick_tmax(int split) {
-  if (split <= 32) return decode_kernel<BF16, HD, GRP, 32>;
-  if (split <= 64) return decode_kernel<BF16, HD, GRP, 64>;
-  if (split <= 128) return decode_kernel<BF16, HD, GRP, 128>;
-  return decode_kernel<BF16, HD, GRP, 256>;
+static decode_fn pick_np(int np) {
+  if (np <= 2) return decode_kernel<BF16, HD, GRP, 2>;
+  if (np <= 4) return decode_kernel<BF16, HD, GRP, 4>;
+  return decode_kernel<BF16, HD, GRP, 8>;
 }
 
 template <bool BF16, int HD>
-static decode_fn pick_grp(int grp, int split) {
+static decode_fn pick_grp(int grp, int np) {
   switch (grp) {
-    case 1: return pick_tmax<BF16, HD, 1>(split);
-    case 2: return pick_tmax<BF16, HD, 2>(split);
-    case 4: return pick_tmax<BF16, HD, 4>(split);
-    default: return pick_tmax<BF16, HD, 8>(split);
+    case 1: return pick_np<BF16, HD, 1>(np);
+    case 2: return pick_np<BF16, HD, 2>(np);
+    case 4: return pick_np<BF16, HD, 4>(np);
+    default: return pick_np<BF16, HD, 8>(np < 4 ? np : 4);
   }
 }
+
+// Longest chunk one workgroup takes: its row offsets live in LDS (8 B each).
+constexpr int kMaxSplit = 4096;
 
 static int64_t n_splits(int32_t cap, int32_t split) { return (int64_t(cap) + split - 1) / split; }
 
@@ -304,11 +442,8 @@ extern "C" int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t he
                                              int32_t cap, int32_t split) {
   if (n_q < 0 || hq < 1 || head_dim < 1 || cap < 1 || split < 1)
     return fail(DA_EINVAL, "workspace sizing: invalid sizes");
-  const int64_t ns = n_splits(cap, split);
-  if (ns <= 1) return 0;
-  const int64_t rows = int64_t(n_q) * hq * ns;
-  const int64_t o_bytes = ((rows * head_dim * 4) + 255) / 256 * 256;
-  return o_bytes + rows * 2 * 4;
+  clear_error();
+  return ws_layout(n_q, hq, head_dim, n_splits(cap, split)).bytes;
 }
 
 extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q, int32_t hq,
@@ -326,27 +461,36 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
   const int grp = hq / hkv;
   if (grp != 1 && grp != 2 && grp != 4 && grp != 8)
     return fail(DA_ENOTSUP, "hq/hkv=%d not in {1, 2, 4, 8}", grp);
-  if (split > 256) return fail(DA_ENOTSUP, "split=%d > 256", split);
+  if (split > kMaxSplit) return fail(DA_ENOTSUP, "split=%d > %d", split, kMaxSplit);
   if (kv->block_table) {
     if (!is_pow2(kv->page_size)) return fail(DA_EINVAL, "page_size=%d not a power of two", kv->page_size);
     if (kv->bt_stride < 1) return fail(DA_EINVAL, "bt_stride=%d < 1", kv->bt_stride);
   }
   if (kv->page_stride < 0 || kv->head_stride < 0 || kv->slot_stride < 0)
     return fail(DA_EINVAL, "negative cache stride");
+  if (kv->n_seq < 1 || kv->n_pages < 1 || kv->max_len < 1)
+    return fail(DA_EINVAL, "cache extents n_seq=%d n_pages=%d max_len=%d must be >= 1",
+                kv->n_seq, kv->n_pages, kv->max_len);
+  if (kv->block_table && (int64_t)kv->max_len > (int64_t)kv->bt_stride * kv->page_size)
+    return fail(DA_EINVAL, "max_len=%d exceeds bt_stride * page_size", kv->max_len);
+  if (!kv->block_table && kv->n_pages < kv->n_seq)
+    return fail(DA_EINVAL, "contiguous cache: n_pages must cover n_seq");
   if (n_q > 0 && (!q || !out || !seq || !count || !idx || !kv->k || !kv->v))
     return fail(DA_EINVAL, "q, out, seq, count, idx, kv->k and kv->v must be non-NULL");
   const int esz = dtype == DA_BF16 ? 2 : 4;
   if (((kv->page_stride | kv->head_stride | kv->slot_stride) * esz) % 16 ||
       ((uintptr_t)kv->k | (uintptr_t)kv->v | (uintptr_t)q | (uintptr_t)out) % 16)
     return fail(DA_EINVAL, "cache rows, q and out must be 16-byte aligned");
-  const int64_t need = da_decode_workspace_bytes(n_q, hq, head_dim, cap, split);
-  if (need > 0 && (!workspace || ws_bytes < need))
-    return fail(DA_ECAPACITY, "workspace %lld bytes < %lld needed", (long long)ws_bytes, (long long)need);
-  if (need > 0 && (uintptr_t)workspace % 256) return fail(DA_EINVAL, "workspace not 256-byte aligned");
+  const int64_t ns = n_splits(cap, split);
+  const WsLayout wl = ws_layout(n_q, hq, head_dim, ns);
+  if (wl.bytes > 0 && (!workspace || ws_bytes < wl.bytes))
+    return fail(DA_ECAPACITY, "workspace %lld bytes < %lld needed", (long long)ws_bytes, (long long)wl.bytes);
+  if (wl.bytes > 0 && (uintptr_t)workspace % 256) return fail(DA_EINVAL, "workspace not 256-byte aligned");
+  const int64_t blocks = int64_t(n_q) * hkv * ns;
+  if (blocks > 0x7fffffff) return fail(DA_ENOTSUP, "grid of %lld workgroups too large", (long long)blocks);
   clear_error();
   if (n_q == 0) return DA_OK;
 
-  const int64_t ns = n_splits(cap, split);
   DecodeArgs a;
   a.q = q;
   a.k = kv->k;
@@ -357,7 +501,10 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
   a.block_table = kv->block_table;
   a.bt_stride = kv->bt_stride;
   a.ps_shift = kv->block_table ? ilog2(kv->page_size) : 0;
-  a.ps_mask = kv->block_table ? kv->page_size - 1 : 0;
+  a.ps_mask = kv->block_table ? kv->page_size - 1 : 0x7fffffff;
+  a.n_seq = kv->block_table ? kv->n_seq : kv->n_pages;
+  a.n_pages = kv->n_pages;
+  a.max_len = kv->max_len;
   a.seq = seq;
   a.count = count;
   a.idx = idx;
@@ -370,29 +517,28 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
   a.qscale = scale * kLog2e;
   a.out = out;
   a.lse = lse;
-  const int64_t rows = int64_t(n_q) * hq * ns;
-  a.ws_o = need > 0 ? reinterpret_cast<float*>(workspace) : nullptr;
-  a.ws_ml = need > 0 ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                                ((rows * head_dim * 4) + 255) / 256 * 256)
-                     : nullptr;
+  char* ws = reinterpret_cast<char*>(workspace);
+  a.ws_o = wl.bytes ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
+  a.ws_ml = wl.bytes ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
 
-  const int64_t blocks = int64_t(n_q) * hkv * ns;
-  if (blocks > 0x7fffffff) return fail(DA_ENOTSUP, "grid of %lld workgroups too large", (long long)blocks);
+  // tile depth: the smallest NP whose two in-flight tiles cover the chunk
+  const int chunk = split < cap ? split : cap;
+  const int rpp = 256 / (head_dim * esz / 16);
+  const int want = (chunk + 2 * rpp - 1) / (2 * rpp);
+  const int np = want <= 2 ? 2 : (want <= 4 ? 4 : 8);
   decode_fn dk;
   merge_fn mk;
   if (dtype == DA_BF16) {
-    dk = head_dim == 64 ? pick_grp<true, 64>(grp, split) : pick_grp<true, 128>(grp, split);
+    dk = head_dim == 64 ? pick_grp<true, 64>(grp, np) : pick_grp<true, 128>(grp, np);
     mk = head_dim == 64 ? merge_kernel<true, 64> : merge_kernel<true, 128>;
   } else {
-    dk = head_dim == 64 ? pick_grp<false, 64>(grp, split) : pick_grp<false, 128>(grp, split);
+    dk = head_dim == 64 ? pick_grp<false, 64>(grp, np) : pick_grp<false, 128>(grp, np);
     mk = head_dim == 64 ? merge_kernel<false, 64> : merge_kernel<false, 128>;
   }
-  hipLaunchKernelGGL(dk, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+  const size_t lds = (size_t)chunk * sizeof(int64_t);
+  hipLaunchKernelGGL(dk, dim3((unsigned)blocks), dim3(256), lds, (hipStream_t)stream, a);
   int rc = check_launch("decode_kernel");
-  if (rc) return rc;
-  if (ns > 1) {
-    hipLaunchKernelGGL(mk, dim3((unsigned)(int64_t(n_q) * hq)), dim3(64), 0, (hipStream_t)stream, a);
-    rc = check_launch("merge_kernel");
-  }
-  return rc;
+  if (rc || ns <= 1) return rc;
+  hipLaunchKernelGGL(mk, dim3((unsigned)(int64_t(n_q) * hq)), dim3(64), 0, (hipStream_t)stream, a);
+  return check_launch("merge_kernel");
 }

@@ -1,0 +1,457 @@
+"""Benchmark of the sparse decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = keep-set build + sparse decode attention (plus the chunk merge
+when a keep-set spans several chunks) for one batch of the LlamaGen-like
+decode workload: 16 requests x 32 heads, head_dim 128, bf16 KV, prompt 120
+tokens, 32x32 raster grid, W = 3 rows, B = 2, row-diagonal mode.  Inputs are
+seeded synthetic tensors, resident in HBM before timing starts.
+
+Cold-cache timing: the KV cache is replicated on the device and step k reads
+copy k mod n, with n chosen so that at least 1 GiB of other kept rows is
+read between two uses of a copy; the kept rows are then not served from the
+4 MB L2s or the 256 MB Infinity Cache, and the reported GB/s is HBM
+bandwidth.  A warm (single copy) figure is reported beside it.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, AMD public spec
+METRIC = "sparse decode-attn tokens/s + kept-KV GB/s vs HBM peak; speedup vs dense"
+ROTATE_BYTES = 1 << 30          # distinct kept bytes between reuses of a copy
+MAX_COPY_BYTES = 48 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kv_bytes_per_key(cfg):
+    esz = 2 if cfg.dtype == "bf16" else 4
+    return cfg.hkv * 2 * cfg.hd * esz        # K and V rows of every kv head
+
+
+class DecodeBench:
+    """Device-resident inputs of one decode workload plus rotation copies."""
+
+    def __init__(self, cfg, n_copies=None, split=None):
+        import torch
+        import ar_image_generation_amd as da
+        import workloads as wl
+        self.torch, self.da = torch, da
+        self.cfg = cfg
+        self.split = split or cfg.split
+        t0 = time.time()
+        self.inp = wl.decode_inputs(cfg)
+        log(f"[bench] {cfg.name}: inputs generated in {time.time() - t0:.1f}s")
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        inp = self.inp
+        self.q = inp.q.to(dev)
+        self.pos = inp.pos.to(dev)
+        self.prompt = inp.prompt_len.to(dev)
+        self.paged = cfg.page_size > 0
+        k = (inp.k_cache if self.paged else inp.k_logical)
+        v = (inp.v_cache if self.paged else inp.v_logical)
+        copy_bytes = 2 * k.numel() * k.element_size()
+        self.copy_bytes = copy_bytes
+        self.n_q = inp.n_q
+        self.hosts = (inp.pos.numpy(), inp.prompt_len.numpy())
+        self.lists = {}
+        self.kept = {}
+        for mode in set(cfg.modes) | {da.DENSE}:
+            m = da.mask(mode, cfg.W, cfg.B, cfg.G)
+            counts = [da.keep_count(m, int(p), int(P)) for p, P in zip(*self.hosts)]
+            cap = max(counts)
+            count = torch.empty(self.n_q, dtype=torch.int32, device=dev)
+            idx = torch.empty((self.n_q, cap), dtype=torch.int32, device=dev)
+            self.lists[mode] = (m, cap, count, idx)
+            self.kept[mode] = sum(counts)
+        sparse_mode = cfg.modes[0]
+        if n_copies is None:
+            kept_b = self.kept[sparse_mode] * kv_bytes_per_key(cfg)
+            n_copies = max(2, math.ceil(ROTATE_BYTES / kept_b))
+            n_copies = min(n_copies, max(2, MAX_COPY_BYTES // copy_bytes))
+        self.n_copies = n_copies
+        t0 = time.time()
+        kd, vd = k.to(dev), v.to(dev)
+        self.k = kd.repeat(n_copies, 1, 1, 1)
+        self.v = vd.repeat(n_copies, 1, 1, 1)
+        del kd, vd
+        seq = inp.seq.to(dev)
+        self.seqs, self.bts = [], []
+        for c in range(n_copies):
+            if self.paged:
+                n_pages = k.shape[0]
+                self.seqs.append(seq)
+                self.bts.append((inp.block_table + c * n_pages).to(dev).contiguous())
+            else:
+                self.seqs.append(seq + c * cfg.n_seq)
+                self.bts.append(None)
+        self.out = torch.empty_like(self.q)
+        self.ws = {}
+        self.splits = {mode: (cfg.dense_split if mode == da.DENSE else self.split)
+                       for mode in self.lists}
+        for mode, (m, cap, count, idx) in self.lists.items():
+            self.ws[mode] = da.decode_workspace(self.n_q, cfg.hq, cfg.hd, cap, self.splits[mode], dev)
+            self.build(mode)            # lists are valid from construction on
+        torch.cuda.synchronize()
+        log(f"[bench] {cfg.name}: {n_copies} cache copies ({n_copies * copy_bytes / 2**30:.1f} GiB) "
+            f"on device in {time.time() - t0:.1f}s")
+
+    def build(self, mode):
+        m, cap, count, idx = self.lists[mode]
+        self.da.keepset_build(m, self.pos, self.prompt, cap, count=count, idx=idx)
+
+    def decode(self, mode, c):
+        m, cap, count, idx = self.lists[mode]
+        self.da.sparse_decode_attn(self.q, self.k, self.v, self.seqs[c], count, idx,
+                                   split=self.splits[mode], block_table=self.bts[c],
+                                   out=self.out, workspace=self.ws[mode])
+
+    def kept_bytes(self, mode):
+        return self.kept[mode] * kv_bytes_per_key(self.cfg)
+
+    def time_graph(self, mode, steps, warmup, with_build=True, rotate=True):
+        """Runs `warmup` eager steps, captures `steps` steps in one HIP graph,
+        replays it once untimed and once timed (events on the capture
+        stream).  Returns microseconds per step.  with_build=False captures
+        decode launches only (the decode kernel's average duration)."""
+        torch = self.torch
+        n = self.n_copies if rotate else 1
+        for w in range(warmup):
+            if with_build:
+                self.build(mode)
+            self.decode(mode, w % n)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(steps):
+                if with_build:
+                    self.build(mode)
+                self.decode(mode, (warmup + s) % n)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        stream = torch.cuda.current_stream()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        del g
+        return us
+
+    def time_eager(self, mode, steps, warmup):
+        """Steps launched one by one from Python (includes host dispatch)."""
+        torch = self.torch
+        n = self.n_copies
+        for w in range(warmup):
+            self.build(mode)
+            self.decode(mode, w % n)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            self.build(mode)
+            self.decode(mode, s % n)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / steps
+
+
+def cpu_baseline(cfg, budget_s=12.0):
+    """The oracle, as it stands, on the same workload: all queries of the
+    batch, repeated until about `budget_s` seconds of CPU work."""
+    import numpy as np
+    import oracle as O
+    import workloads as wl
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    inp = wl.decode_inputs(cfg)
+    args = (inp.q.double().numpy(), inp.k_logical.double().numpy(), inp.v_logical.double().numpy(),
+            inp.pos.numpy(), inp.prompt_len.numpy(), inp.seq.numpy())
+    mode = cfg.modes[0]
+    done, t0 = 0, time.time()
+    while True:
+        O.decode_attention(*args, W=cfg.W, B=cfg.B, G=cfg.G, mode=mode)
+        done += 1
+        if time.time() - t0 >= budget_s:
+            break
+    dt = time.time() - t0
+    return {"value": round(done * inp.n_q / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} pass(es) over all {inp.n_q} queries x {cfg.hq} heads of {cfg.name} "
+                      f"({O.__name__} fp64 numpy, {dt:.1f}s wall)"}
+
+
+def traffic_from_profile(workload):
+    """HBM bytes per launch of the decode kernel from the committed
+    rocprofv3 counter summary, or None when there is none or the kernel
+    source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_sha256") != kernel_sha(DECODE_SRC):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+DECODE_SRC = [os.path.join(ROOT, "ar_image_generation_amd", "csrc", f)
+              for f in ("decode.hip", "common.h")]
+PROBE_BYTES = 256 << 20
+
+
+def profile_run(args):
+    """Only the timed launches (for rocprofv3): K cold steps of the headline
+    workload, then one streaming-read probe of PROBE_BYTES (the counter
+    calibration: a read of known size)."""
+    import torch
+    import workloads as wl
+    import ar_image_generation_amd as da
+    cfg = wl.CONFIGS[args.workload]
+    b = DecodeBench(cfg, split=args.split)
+    us = b.time_graph(cfg.modes[0], args.steps, args.warmup)
+    buf = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(4096, dtype=torch.int32, device="cuda")
+    da.hbm_read_probe(buf, sink, 2048)
+    torch.cuda.synchronize()
+    log(f"[bench] profile run: {us:.2f} us/step; probe {PROBE_BYTES} bytes")
+
+
+def summarize(args):
+    """Writes profiles/decode_<workload>.txt from three rocprofv3 runs of
+    `bench.py --profile-run`: --kernel-trace, --pmc FETCH_SIZE, --pmc WRITE_SIZE."""
+    import csv
+    import workloads as wl
+    import ar_image_generation_amd as da
+    cfg = wl.CONFIGS[args.workload]
+    trace_dir, fetch_dir, write_dir = args.summarize
+
+    def rows(d, suffix):
+        import glob
+        out = []
+        for f in glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    def decode_rows(rs):
+        return [r for r in rs if "decode_kernel" in r.get("Kernel_Name", "")]
+
+    tr = decode_rows(rows(trace_dir, "kernel_trace.csv"))
+    durs = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr)
+    kname = tr[0]["Kernel_Name"] if tr else "?"
+    ks = [r for r in rows(trace_dir, "kernel_trace.csv") if "keepset_kernel" in r["Kernel_Name"]]
+    kdur = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in ks)
+
+    def counter(d, name):
+        per = {}
+        for r in rows(d, "counter_collection.csv"):
+            if r.get("Counter_Name") != name:
+                continue
+            per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), 0.0)
+            per[(r["Kernel_Name"], r["Dispatch_Id"])] += float(r["Counter_Value"])
+        dec = [v for (k, _), v in per.items() if "decode_kernel" in k]
+        probe = [v for (k, _), v in per.items() if "read_probe_kernel" in k]
+        # the probe buffer's fill: a plain write kernel of PROBE_BYTES
+        fill = [v for (k, _), v in per.items() if "FillFunctor<int>" in k]
+        return (sum(dec) / len(dec) if dec else None, probe[-1] if probe else None,
+                max(fill) if fill else None)
+
+    f_dec, f_probe, _ = counter(fetch_dir, "FETCH_SIZE")
+    w_dec, _, w_fill = counter(write_dir, "WRITE_SIZE")
+    scale = (PROBE_BYTES / 1024.0) / f_probe if f_probe else None
+    wscale = (PROBE_BYTES / 1024.0) / w_fill if w_fill else None
+    m = da.mask(cfg.modes[0], cfg.W, cfg.B, cfg.G)
+    pos, prompt, _ = wl.positions(cfg)
+    kept = sum(da.keep_count(m, int(p), int(P)) for p, P in zip(pos.tolist(), prompt.tolist()))
+    kept_bytes = kept * kv_bytes_per_key(cfg)
+    hbm = None
+    if f_dec is not None and scale is not None and w_dec is not None and wscale is not None:
+        hbm = (f_dec * scale + w_dec * wscale) * 1024.0
+    avg = sum(durs) / len(durs) if durs else float("nan")
+    lines = [
+        f"# rocprofv3 summary: sparse decode kernel, workload {cfg.name}",
+        "# commands (repo root, TMPDIR=/tmp):",
+        f"#   rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o run -- python3 bench.py --profile-run --steps {args.steps} --warmup {args.warmup}",
+        f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o run -- python3 bench.py --profile-run --steps {args.steps} --warmup {args.warmup}",
+        f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o run -- python3 bench.py --profile-run --steps {args.steps} --warmup {args.warmup}",
+        f"#   python3 bench.py --summarize {trace_dir} {fetch_dir} {write_dir}",
+        f"kernel = {kname}",
+        f"dispatches = {len(durs)}",
+        f"avg_duration_us = {avg / 1e3:.3f}",
+        f"median_duration_us = {durs[len(durs) // 2] / 1e3 if durs else float('nan'):.3f}",
+        f"min_duration_us = {durs[0] / 1e3 if durs else float('nan'):.3f}",
+        f"keepset_kernel_avg_us = {sum(kdur) / len(kdur) / 1e3 if kdur else float('nan'):.3f}",
+        f"kept_bytes_per_launch = {kept_bytes}",
+        f"achieved_GBps_from_avg = {kept_bytes / avg if durs else float('nan'):.1f}",
+        f"fetch_kib_per_dispatch = {f_dec}",
+        f"write_kib_per_dispatch = {w_dec}",
+        f"probe_fetch_kib = {f_probe} (read of {PROBE_BYTES} bytes)",
+        f"fetch_scale = {scale}",
+        f"write_calibration_kib = {w_fill} (fill of {PROBE_BYTES} bytes)",
+        f"write_scale = {wscale}",
+        f"hbm_bytes_per_launch = {hbm}",
+        f"traffic_over_kept = {hbm / kept_bytes if hbm else None}",
+        f"kernel_sha256 = {kernel_sha(DECODE_SRC)}",
+    ]
+    out = os.path.join(ROOT, "profiles", f"decode_{cfg.name}_traffic.txt")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llamagen_b16")
+    ap.add_argument("--split", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="run only the timed decode launches and one probe (for rocprofv3)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the profiles/ summary from three rocprofv3 output folders")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path is data-parallel over requests "
+              "and heads with no exchange, and this build runs on a single MI355X. "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.profile_run:
+        profile_run(args)
+        return
+
+    import torch
+    import workloads as wl
+    import ar_image_generation_amd as da
+    da.load()
+    props = torch.cuda.get_device_properties(0)
+    log(f"[bench] device: {props.name} {getattr(props, 'gcnArchName', '')} "
+        f"CUs={props.multi_processor_count}")
+
+    cfg = wl.CONFIGS[args.workload]
+    b = DecodeBench(cfg, split=args.split)
+    mode = cfg.modes[0]
+    K, W = args.steps, args.warmup
+    us_step = b.time_graph(mode, K, W)
+    us_dec = b.time_graph(mode, K, W, with_build=False)
+    us_dec_warm = b.time_graph(mode, K, W, with_build=False, rotate=False)
+    us_step_d = b.time_graph(da.DENSE, K, W)
+    us_dec_d = b.time_graph(da.DENSE, K, W, with_build=False)
+    us_eager = b.time_eager(mode, K, W)
+    log(f"[bench] {cfg.name} sparse: {us_step:.2f} us/step (graph), {us_eager:.2f} us/step eager, "
+        f"decode {us_dec:.2f} us cold / {us_dec_warm:.2f} us warm; dense {us_step_d:.2f} us/step, "
+        f"decode {us_dec_d:.2f} us")
+
+    kept = b.kept_bytes(mode)
+    achieved = kept / (us_dec * 1e-6) / 1e9
+    value = b.n_q / (us_step * 1e-6)
+    traffic = traffic_from_profile(cfg.name)
+
+    extra = {}
+    if not args.no_extra:
+        for name in ("gqa_b64", "paged_b128"):
+            c = wl.CONFIGS[name]
+            eb = DecodeBench(c)
+            rec = {}
+            for md in list(dict.fromkeys(list(c.modes) + [da.DENSE])):
+                st = eb.time_graph(md, K, W)
+                dk = eb.time_graph(md, K, W, with_build=False)
+                gbps = eb.kept_bytes(md) / (dk * 1e-6) / 1e9
+                rec[wl.MODE_NAMES[md]] = {
+                    "us_per_step": round(st, 2), "decode_us": round(dk, 2),
+                    "tokens_per_s": round(eb.n_q / (st * 1e-6), 1),
+                    "kept_MB": round(eb.kept_bytes(md) / 1e6, 2),
+                    "kept_GBps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+                log(f"[bench] {name} {wl.MODE_NAMES[md]}: {st:.2f} us/step, decode "
+                    f"{dk:.2f} us, {gbps:.0f} GB/s")
+            dense_us = rec["dense"]["decode_us"]
+            for md in c.modes:
+                r = rec[wl.MODE_NAMES[md]]
+                r["speedup_vs_dense"] = round(dense_us / r["decode_us"], 3)
+            extra[name] = rec
+            del eb
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        cpu = cpu_baseline(cfg)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_step * 1e-3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded correlated-field K/V, random positions)",
+        "config": {"workload": cfg.name, "requests": cfg.n_seq, "q_heads": cfg.hq,
+                   "kv_heads": cfg.hkv, "head_dim": cfg.hd, "prompt": cfg.prompt[0],
+                   "grid": cfg.G, "W": cfg.W, "B": cfg.B, "mode": wl.MODE_NAMES[mode],
+                   "split": b.split, "dense_split": cfg.dense_split, "cache_copies": b.n_copies,
+                   "step": "keepset_build + sparse_decode_attn, HIP graph of K steps"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "decode_us": round(us_dec, 3),
+        "kept_MB_per_step": round(kept / 1e6, 3),
+        "eager_us_per_step": round(us_eager, 2),
+        "warm": {"decode_us": round(us_dec_warm, 2),
+                 "kept_GBps": round(kept / (us_dec_warm * 1e-6) / 1e9, 1)},
+        "dense": {"us_per_step": round(us_step_d, 2), "decode_us": round(us_dec_d, 2),
+                  "kept_MB": round(b.kept_bytes(da.DENSE) / 1e6, 2),
+                  "speedup_step": round(us_step_d / us_step, 3),
+                  "speedup_decode": round(us_dec_d / us_dec, 3)},
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -121,7 +121,13 @@ int da_keepset_build(const da_mask* m /* [host] */, int32_t n_q,
  * (a contiguous [n_seq][hkv][Lmax][head_dim] cache has
  * page_stride = hkv*Lmax*hd, head_stride = Lmax*hd, slot_stride = hd).
  * Strides are in elements; head_dim elements of one row are contiguous and
- * 16-byte aligned.  page_size must be a power of two when block_table is set. */
+ * 16-byte aligned.  page_size must be a power of two when block_table is set.
+ * Extents: n_seq requests (rows of the block table; with no table, requests
+ * in the cache), n_pages pages in k/v (with no table: = n_seq), max_len
+ * logical positions per request (<= bt_stride * page_size with a table).
+ * The kernels clamp every request, position and page index they read from
+ * device memory into these extents, so inconsistent device-side lists give
+ * wrong numbers, never an out-of-bounds access. */
 typedef struct {
   const void* k;
   const void* v;
@@ -131,10 +137,14 @@ typedef struct {
   int32_t page_size;
   int32_t bt_stride;
   const int32_t* block_table;   /* [n_seq][bt_stride] or NULL */
+  int32_t n_seq;
+  int32_t n_pages;
+  int32_t max_len;
 } da_kv_cache;
 
 /* [host] Workspace bytes da_sparse_decode_attn needs for these sizes (0 when
- * every keep-set fits one split, i.e. cap <= split). */
+ * every keep-set fits one chunk, i.e. cap <= split): the per-chunk partial
+ * results (max, sum, unnormalised output) that the merge kernel combines. */
 int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t head_dim,
                                   int32_t cap, int32_t split);
 
@@ -149,28 +159,40 @@ int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t head_dim,
  *
  * Work split: each query's list is cut into chunks of `split` keys; each
  * (query, kv head, chunk) is one workgroup that serves all hq/hkv query heads
- * of the kv head, so each kept K/V row is read from HBM once.  Chunks are
- * combined by a log-sum-exp merge (a second kernel, only when cap > split).
+ * of the kv head, so each kept K/V row is read from HBM once.  When a list
+ * spans several chunks (cap > split), a second kernel combines the chunk
+ * partials by a log-sum-exp merge.
  *
  *   q     [n_q][hq][head_dim] in `dtype`
  *   out   [n_q][hq][head_dim] in `dtype`
  *   lse   [n_q][hq] fp32 natural-log sum of exp of the scaled logits, or NULL
  *   seq   [n_q] request (block-table row) of each query
  *   count [n_q], idx [n_q][cap] as written by da_keepset_build
- *   workspace: da_decode_workspace_bytes(...) bytes, 256-byte aligned, or NULL
- *         when that is 0; its contents need no initialisation.
- * Preconditions on device data: 1 <= count[q] (counts above cap are read as
- * cap); every listed position addresses a valid cache row of request seq[q].
+ *   workspace: da_decode_workspace_bytes(...) bytes, 256-byte aligned, or
+ *         NULL when that is 0; no initialisation needed.  Calls that share a
+ *         workspace must not overlap in time (one workspace per stream).
+ * Device data: counts above cap are read as cap; a query with count 0 gets
+ * no output written.  Listed positions, seq[] and block-table entries are
+ * clamped into the descriptor's extents (see da_kv_cache).
  * Errors: DA_EINVAL (null pointers, n_q < 0, hq or hkv < 1, hq % hkv != 0,
  * cap < 1, split < 1, non-power-of-two page_size with a block table,
- * bt_stride < 1), DA_ENOTSUP (head_dim not 64/128, dtype, hq/hkv not in
- * {1,2,4,8}, split > 256), DA_ECAPACITY (workspace too small). */
+ * bt_stride < 1, extents < 1, max_len > bt_stride * page_size), DA_ENOTSUP (head_dim not 64/128, dtype, hq/hkv not in
+ * {1,2,4,8}, split > 4096), DA_ECAPACITY (workspace too small). */
 int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
                           int32_t hq, int32_t hkv, int32_t head_dim, float scale,
                           const da_kv_cache* kv /* [host] */, const int32_t* seq,
                           const int32_t* count, const int32_t* idx, int32_t cap,
                           int32_t split, void* out, float* lse,
                           void* workspace, int64_t ws_bytes, void* stream);
+
+/* Measurement: streaming read of `bytes` bytes at `buf` (16-byte aligned, a
+ * multiple of 16) by `grid` workgroups of 256 threads, 16-byte loads, eight
+ * in flight per thread; writes one word per workgroup to sink[grid].  Its
+ * bytes / duration is the attainable HBM read bandwidth that decode's
+ * kept-byte bandwidth is compared with.  Errors: DA_EINVAL for NULL
+ * pointers, a bad size or alignment, grid < 1. */
+int da_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid,
+                      void* stream);
 
 #ifdef __cplusplus
 }

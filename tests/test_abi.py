@@ -83,7 +83,7 @@ def test_argument_errors_are_reported_before_launch():
     # zero queries is a valid no-op
     assert lib.da_keepset_build(m, 0, None, None, 0, 4, None, None, 0, None, None, None) == 0
 
-    kv = _native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None)
+    kv = _native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None, 1, 1, 8)
 
     def dec(dtype=1, n_q=1, hq=8, hkv=2, hd=128, cap=64, split=64, ws=None, wsb=0, kvd=kv, q=dummy):
         return lib.da_sparse_decode_attn(q, dtype, n_q, hq, hkv, hd, 0.1, kvd, dummy, dummy,
@@ -93,11 +93,15 @@ def test_argument_errors_are_reported_before_launch():
     assert dec(dtype=3) == -2
     assert dec(hq=48, hkv=3) == -2          # group 16
     assert dec(split=0) == -1
-    assert dec(split=300) == -2
+    assert dec(split=5000) == -2
     assert dec(cap=200, split=64) == -3     # needs a workspace
     assert "workspace" in _native.last_error()
-    paged = _native.DaKvCache(16, 16, 0, 0, 0, 12, 4, 16)
+    paged = _native.DaKvCache(16, 16, 0, 0, 0, 12, 4, 16, 1, 4, 48)
     assert dec(kvd=paged) == -1 and "power of two" in _native.last_error()
+    paged = _native.DaKvCache(16, 16, 0, 0, 0, 16, 4, 16, 1, 4, 65)
+    assert dec(kvd=paged) == -1 and "max_len" in _native.last_error()
+    assert dec(kvd=_native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None, 1, 1, 0)) == -1
+    assert dec(kvd=_native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None, 3, 2, 8)) == -1
     assert dec(q=ctypes.c_void_p(8)) == -1   # misaligned q
 
 

@@ -34,7 +34,8 @@ class DecodeConfig:
     kv_gen: str = "normal"  # "normal" | "field"
     seed: int = 0
     queries_per_seq: int = 1
-    split: int = 64         # listed keys per decode workgroup (launch setting)
+    split: int = 4096       # listed keys per decode workgroup, sparse masks (launch setting)
+    dense_split: int = 512  # the same for the dense all-keep run
 
     @property
     def n_vis(self) -> int:
