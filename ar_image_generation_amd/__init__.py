@@ -7,6 +7,7 @@ from .api import (  # noqa: F401
     BAND,
     DENSE,
     ROWDIAG,
+    band_prefill_attn,
     decode_workspace,
     decode_workspace_bytes,
     hbm_read_probe,

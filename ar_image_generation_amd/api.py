@@ -13,6 +13,8 @@ from typing import Optional
 
 import torch
 
+from ctypes import c_int64 as ctypes_i64
+
 from ._native import DaKvCache, DaMask, check, load
 
 DENSE, BAND, ROWDIAG = 0, 1, 2
@@ -167,3 +169,35 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int,
     check(load().da_hbm_read_probe(buf.data_ptr() + offset, nbytes, sink.data_ptr(), grid,
                                    _stream(buf)),
           "da_hbm_read_probe")
+
+
+def band_prefill_attn(m: DaMask, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                      prompt_len: torch.Tensor, *, scale: Optional[float] = None, out=None,
+                      lse=None, want_lse: bool = False):
+    """q [batch, heads, n, hd], k/v [batch, kv_heads, n, hd] bf16 (head_dim
+    contiguous); prompt_len [batch] int32.  Returns (out, lse or None)."""
+    _need_cuda("band_prefill_attn", q, k, v, prompt_len)
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be [batch, heads, n, hd] and k, v [batch, kv_heads, n, hd]")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("band_prefill_attn takes bf16 tensors")
+    bsz, heads, n, hd = q.shape
+    if k.shape[0] != bsz or k.shape[2] != n or k.shape[3] != hd:
+        raise ValueError("k/v shape does not match q")
+    if prompt_len.dtype != torch.int32 or prompt_len.numel() != bsz:
+        raise ValueError("prompt_len must be int32 [batch]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(hd)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((bsz, heads, n), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, out):
+        if t.stride(3) != 1:
+            raise ValueError("head_dim must be contiguous")
+    st = (ctypes_i64 * 12)(*[t.stride(d) for t in (q, k, v, out) for d in (0, 1, 2)])
+    check(load().da_band_prefill_attn(m, 1, bsz, heads, k.shape[1], n, hd, _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(out), st, _ptr(prompt_len), float(scale),
+                                      _ptr(lse), _stream(q)),
+          "da_band_prefill_attn")
+    return out, lse

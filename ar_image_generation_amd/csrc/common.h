@@ -39,6 +39,8 @@ __host__ __device__ inline bool window_keep(int mode, int d, int B, int G) {
 
 // ---------------------------------------------------------------- device side
 
+__device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
 // 16-byte vector of raw bits (8 bf16 or 4 fp32).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

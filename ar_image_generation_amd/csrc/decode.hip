@@ -67,7 +67,6 @@ static WsLayout ws_layout(int64_t n_q, int64_t hq, int64_t hd, int64_t ns) {
   return w;
 }
 
-__device__ inline int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 template <bool BF16, int EPL>
 __device__ inline void store_out(void* base, int64_t off, const float* x) {

@@ -185,6 +185,34 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
                           int32_t split, void* out, float* lse,
                           void* workspace, int64_t ws_bytes, void* stream);
 
+/* band_prefill_attn -- keep-set-masked causal attention over whole sequences
+ * (prefill), on the matrix cores.
+ *
+ * For every batch b, query head h and row i < n:
+ *   out[b][h][i][:] = sum_j w_ij v[b][hk][j][:],
+ *   w_i = softmax over kept keys j <= i of scale * q[b][h][i] . k[b][hk][j],
+ * with the keep rule above for a query at position i and prompt_len[b]
+ * prompt tokens, hk = h / (heads / kv_heads).  This is the summary's masked
+ * softmax (core formulas) applied to every row of the sequence; the pages
+ * apply the sparsity to decode, and this call serves the same mask where a
+ * whole sequence is attended at once.
+ *
+ *   q, out [batch][heads][n][head_dim], k, v [batch][kv_heads][n][head_dim],
+ *          bf16, head_dim elements contiguous and 16-byte aligned;
+ *   strides[12] [host]: element strides (batch, head, position) of q, k, v,
+ *          out, in that order, each a multiple of 8;
+ *   prompt_len [batch] (device; read clamped to [0, n]);
+ *   lse [batch][heads][n] fp32 natural-log sums, or NULL.
+ * Scores accumulate in fp32 from bf16 products; probabilities are rounded to
+ * bf16 for the second product; outputs round to nearest even.
+ * Errors: DA_EINVAL (mask, null pointers, sizes, strides, alignment),
+ * DA_ENOTSUP (causal = 0, dtype other than bf16, head_dim not 64/128). */
+int da_band_prefill_attn(const da_mask* m /* [host] */, da_dtype dtype, int32_t batch,
+                         int32_t heads, int32_t kv_heads, int32_t n, int32_t head_dim,
+                         const void* q, const void* k, const void* v, void* out,
+                         const int64_t* strides /* [host] 12 */, const int32_t* prompt_len,
+                         float scale, float* lse, void* stream);
+
 /* Measurement: streaming read of `bytes` bytes at `buf` (16-byte aligned, a
  * multiple of 16) by `grid` workgroups of 256 threads, 16-byte loads, eight
  * in flight per thread; writes one word per workgroup to sink[grid].  Its

@@ -1,0 +1,122 @@
+"""GPU band-masked prefill (MFMA) vs the fp64 oracle.
+
+bf16 inputs: max |o - ref| <= 2e-2 with the oracle run on the same
+bf16-rounded values; natural-log LSE within 1e-3."""
+import numpy as np
+import pytest
+import torch
+
+import ar_image_generation_amd as da
+import oracle as O
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+ATOL = 2e-2
+
+
+def run(q, k, v, prompt, mode, W, B, G):
+    m = da.mask(mode, W, B, G)
+    out, lse = da.band_prefill_attn(m, q.to(DEV), k.to(DEV), v.to(DEV),
+                                    torch.as_tensor(prompt, dtype=torch.int32).to(DEV),
+                                    want_lse=True)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+def oracle_rows(q, k, v, prompt, mode, W, B, G, rows):
+    heads, kvh = q.shape[1], k.shape[1]
+    rep = heads // kvh
+    K = np.repeat(k.double().numpy(), rep, axis=1)
+    V = np.repeat(v.double().numpy(), rep, axis=1)
+    return O.prefill_attention(q.double().numpy(), K, V, prompt, W=W, B=B, G=G, mode=mode,
+                               rows=rows)
+
+
+def check(out, lse, ref):
+    o = out.double().numpy()
+    l = lse.double().numpy()
+    worst = 0.0
+    for (b, h, i), (ro, rl) in ref.items():
+        err = np.abs(o[b, h, i] - ro).max()
+        worst = max(worst, err)
+        assert err <= ATOL, ((b, h, i), err)
+        assert abs(l[b, h, i] - rl) <= 1e-3 * max(1.0, abs(rl)), ((b, h, i), l[b, h, i], rl)
+    return worst
+
+
+def randn(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode", [O.ROWDIAG, O.BAND, O.DENSE])
+@pytest.mark.parametrize("hd,heads,kvh", [(128, 2, 2), (64, 4, 2)])
+def test_small_all_rows(mode, hd, heads, kvh):
+    """Ragged length (not a tile multiple), window crossing the prompt,
+    GQA heads: every row against the oracle."""
+    P, G, rows_w, B = 20, 16, 4, 3
+    W = rows_w * G
+    n = P + G * G + 7
+    q, k, v = randn((2, heads, n, hd), 1), randn((2, kvh, n, hd), 2), randn((2, kvh, n, hd), 3)
+    prompt = [P, 3]
+    out, lse = run(q, k, v, prompt, mode, W, B, G)
+    rows = [(b, h, i) for b in range(2) for h in range(heads) for i in range(n)]
+    check(out, lse, oracle_rows(q, k, v, prompt, mode, W, B, G, rows))
+
+
+@pytest.mark.parametrize("n,P,W,B,G", [(1, 0, 4, 1, 4), (5, 9, 4, 1, 4), (63, 0, 0, 0, 8),
+                                       (65, 64, 8, 2, 8), (130, 7, 40, 9, 10)])
+def test_edge_shapes(n, P, W, B, G):
+    q, k, v = randn((1, 2, n, 128), 4), randn((1, 2, n, 128), 5), randn((1, 2, n, 128), 6)
+    for mode in (O.ROWDIAG, O.BAND):
+        out, lse = run(q, k, v, [P], mode, W, B, G)
+        rows = [(0, h, i) for h in range(2) for i in range(n)]
+        check(out, lse, oracle_rows(q, k, v, [P], mode, W, B, G, rows))
+
+
+def test_single_kept_key_rows_return_their_value():
+    """P = 0, W = 0, B = 0: each row keeps only its own key."""
+    n = 70
+    q, k, v = randn((1, 2, n, 128), 7), randn((1, 2, n, 128), 8), randn((1, 2, n, 128), 9)
+    out, _ = run(q, k, v, [0], O.BAND, 0, 0, 4)
+    assert torch.equal(out, v)
+
+
+def test_full_prefill_workload_sampled_rows():
+    """The full prefill workload (2 x 32 heads x 4352 tokens, head_dim 128):
+    a seeded sample of rows, including the prompt boundary, the first rows
+    past the window and the last row."""
+    cfg = wl.PREFILL_CONFIGS["prefill_b2"]
+    inp = wl.prefill_inputs(cfg)
+    out, lse = run(inp.q, inp.k, inp.v, inp.prompt_len.tolist(), cfg.mode, cfg.W, cfg.B, cfg.G)
+    assert torch.isfinite(out.float()).all()
+    rng = np.random.default_rng(0)
+    fixed = [0, 1, 63, 64, cfg.P - 1, cfg.P, cfg.P + 1, cfg.P + cfg.W, cfg.P + cfg.W + 1,
+             cfg.n - 1]
+    rows = []
+    for b in range(cfg.batch):
+        for h in rng.choice(cfg.heads, size=6, replace=False):
+            for i in fixed + rng.choice(cfg.n, size=8, replace=False).tolist():
+                rows.append((b, int(h), int(i)))
+    check(out, lse, oracle_rows(inp.q, inp.k, inp.v, inp.prompt_len.tolist(), cfg.mode, cfg.W,
+                                cfg.B, cfg.G, rows))
+
+
+def test_prefill_row_matches_decode_at_that_position():
+    """Row i of prefill and a decode query at position i over the same cache
+    agree (two different kernels, same keep-set)."""
+    P, G, W, B, n = 16, 16, 64, 2, 16 + 256
+    q, k, v = randn((1, 4, n, 128), 10), randn((1, 4, n, 128), 11), randn((1, 4, n, 128), 12)
+    out, _ = run(q, k, v, [P], O.ROWDIAG, W, B, G)
+    pos = torch.arange(n, dtype=torch.int32)
+    m = da.mask(O.ROWDIAG, W, B, G)
+    count, idx, _, _ = da.keepset_build(m, pos.to(DEV), torch.full((n,), P, dtype=torch.int32).to(DEV),
+                                        da.keep_cap(m, n - 1, P))
+    qd = q[0].permute(1, 0, 2).contiguous().to(DEV)          # [n, heads, hd]
+    dec, _ = da.sparse_decode_attn(qd, k.to(DEV), v.to(DEV), torch.zeros(n, dtype=torch.int32).to(DEV),
+                                   count, idx, split=4096)
+    torch.cuda.synchronize()
+    diff = (dec.cpu().float().permute(1, 0, 2) - out[0].float()).abs().max().item()
+    assert diff <= ATOL
