@@ -16,5 +16,6 @@ from .api import (  # noqa: F401
     keepset_build,
     kv_cache,
     mask,
+    prefill_tiles_build,
     sparse_decode_attn,
 )

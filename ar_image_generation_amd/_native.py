@@ -35,9 +35,12 @@ SIGNATURES = {
                                         c_vp, c_vp, c_i32, c_vp, c_vp, c_vp]),
     "da_decode_workspace_bytes": (c_i64, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "da_hbm_read_probe": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i32, c_vp]),
+    "da_prefill_tiles_bytes": (c_i64, [c_i32, c_i32]),
+    "da_prefill_tiles_build": (ctypes.c_int, [ctypes.POINTER(DaMask), c_i32, c_i32, c_vp, c_vp,
+                                              c_i64, c_vp]),
     "da_band_prefill_attn": (ctypes.c_int, [ctypes.POINTER(DaMask), ctypes.c_int, c_i32, c_i32, c_i32,
                                             c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
-                                            ctypes.POINTER(c_i64), c_vp, c_f32, c_vp, c_vp]),
+                                            ctypes.POINTER(c_i64), c_vp, c_vp, c_f32, c_vp, c_vp]),
     "da_sparse_decode_attn": (ctypes.c_int, [c_vp, ctypes.c_int, c_i32, c_i32, c_i32, c_i32, c_f32,
                                              ctypes.POINTER(DaKvCache), c_vp, c_vp, c_vp, c_i32,
                                              c_i32, c_vp, c_vp, c_vp, c_i64, c_vp]),

@@ -171,12 +171,31 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int,
           "da_hbm_read_probe")
 
 
+def prefill_tiles_build(m: DaMask, prompt_len: torch.Tensor, n: int, tiles=None) -> torch.Tensor:
+    """Tile lists of the keep-set for prefill of len(prompt_len) sequences of
+    n tokens (uint8 device buffer in the layout of include/diagattn.h)."""
+    _need_cuda("prefill_tiles_build", prompt_len)
+    if prompt_len.dtype != torch.int32 or not prompt_len.is_contiguous():
+        raise ValueError("prompt_len must be contiguous int32")
+    bsz = prompt_len.numel()
+    nbytes = int(load().da_prefill_tiles_bytes(bsz, n))
+    check(0 if nbytes >= 0 else nbytes, "da_prefill_tiles_bytes")
+    if tiles is None:
+        tiles = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=prompt_len.device)
+    check(load().da_prefill_tiles_build(m, bsz, n, _ptr(prompt_len), _ptr(tiles),
+                                        tiles.numel(), _stream(prompt_len)),
+          "da_prefill_tiles_build")
+    return tiles
+
+
 def band_prefill_attn(m: DaMask, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                      prompt_len: torch.Tensor, *, scale: Optional[float] = None, out=None,
-                      lse=None, want_lse: bool = False):
+                      prompt_len: torch.Tensor, *, tiles: Optional[torch.Tensor] = None,
+                      scale: Optional[float] = None, out=None, lse=None,
+                      want_lse: bool = False):
     """q [batch, heads, n, hd], k/v [batch, kv_heads, n, hd] bf16 (head_dim
-    contiguous); prompt_len [batch] int32.  Returns (out, lse or None)."""
-    _need_cuda("band_prefill_attn", q, k, v, prompt_len)
+    contiguous); prompt_len [batch] int32; tiles from ``prefill_tiles_build``
+    (built here when omitted).  Returns (out, lse or None)."""
+    _need_cuda("band_prefill_attn", q, k, v, prompt_len, tiles)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("q must be [batch, heads, n, hd] and k, v [batch, kv_heads, n, hd]")
     if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
@@ -186,6 +205,10 @@ def band_prefill_attn(m: DaMask, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
         raise ValueError("k/v shape does not match q")
     if prompt_len.dtype != torch.int32 or prompt_len.numel() != bsz:
         raise ValueError("prompt_len must be int32 [batch]")
+    if tiles is None:
+        tiles = prefill_tiles_build(m, prompt_len, n)
+    elif tiles.numel() * tiles.element_size() < load().da_prefill_tiles_bytes(bsz, n):
+        raise ValueError("tiles buffer too small for these sizes")
     if scale is None:
         scale = 1.0 / math.sqrt(hd)
     if out is None:
@@ -197,7 +220,7 @@ def band_prefill_attn(m: DaMask, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
             raise ValueError("head_dim must be contiguous")
     st = (ctypes_i64 * 12)(*[t.stride(d) for t in (q, k, v, out) for d in (0, 1, 2)])
     check(load().da_band_prefill_attn(m, 1, bsz, heads, k.shape[1], n, hd, _ptr(q), _ptr(k),
-                                      _ptr(v), _ptr(out), st, _ptr(prompt_len), float(scale),
-                                      _ptr(lse), _stream(q)),
+                                      _ptr(v), _ptr(out), st, _ptr(prompt_len), _ptr(tiles),
+                                      float(scale), _ptr(lse), _stream(q)),
           "da_band_prefill_attn")
     return out, lse

@@ -37,10 +37,17 @@ struct PrefillArgs {
   float* lse;                       // [batch][heads][n] or null
   int64_t sq[3], sk[3], sv[3], so[3];   // element strides (batch, head, position)
   const int32_t* prompt_len;        // [batch]
-  int batch, heads, kv_heads, n, n_qt;
+  const int32_t* tile_count;        // [batch][n_qt]
+  const int4* tile_list;            // [batch][n_qt][max_tiles] (key tile, need bits, full bits, -)
+  int batch, heads, kv_heads, n, n_qt, max_tiles;
   int mode, W, B, G;
   float qscale;                     // scale * log2(e)
+  float inv_g;                      // 1 / G
 };
+
+// Query tile: 4 waves x RB_MAX row blocks of 16 rows; key tile: BN keys.
+constexpr int RB_MAX = 2;
+constexpr int BM_ROWS = 64 * RB_MAX;
 
 constexpr int BN = 64;              // keys per tile
 constexpr float kLog2eP = 1.4426950408889634f;
@@ -76,42 +83,132 @@ __device__ inline bool keep_pair(int i, int j, int P, int mode, int W, int B, in
   return d <= W && window_keep(mode, d, B, G);
 }
 
-template <int HD, int RB>
-__global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
-  constexpr int BM = 64 * RB;
-  constexpr int NC = HD / 32;        // 32-wide contraction chunks of the head dim
-  constexpr int NB = HD / 16;        // 16-wide output blocks of the head dim
-  constexpr int KSTR = HD + 8;       // LDS row stride of K (elements), padded
-  constexpr int VSTR = BN + 4;       // LDS row stride of V^T (elements), padded
-  constexpr int CPR = HD / 8;        // 16-byte chunks per key row
-  constexpr int LPT = BN * CPR / 256;  // 16-byte chunks per thread per tile (K and V each)
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
-  __shared__ __attribute__((aligned(16))) uint16_t ks[BN * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[HD * VSTR];
+// Non-negative x mod G through a float reciprocal (exact for |x| < 2^22).
+__device__ inline int mod_g(int x, int G, float inv_g) {
+  int r = x - G * (int)floorf((float)x * inv_g);
+  r += r < 0 ? G : 0;
+  r -= r >= G ? G : 0;
+  return r;
+}
+
+// ---------------------------------------------------------------- tile lists
+// For query tile qt of batch b: the key tiles (BN keys) holding a kept pair,
+// in order, each with two 32-bit masks over (wave, row block, 16-key block)
+// -- bit w*8 + rb*4 + kq: that block has a kept pair / every pair is kept.
+// One wave per (b, qt); lane = candidate key tile; a ballot keeps the order.
+__global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x / a.n_qt;
+  const int qt = blockIdx.x % a.n_qt;
+  const int n = a.n;
+  const int P = clampi(a.prompt_len[b], 0, n);
+  const int i0 = qt * BM_ROWS;
+  const int i_last = i0 + BM_ROWS - 1 < n - 1 ? i0 + BM_ROWS - 1 : n - 1;
+  int4* out = const_cast<int4*>(a.tile_list) + ((int64_t)b * a.n_qt + qt) * a.max_tiles;
+  int count = 0;
+  const int jt_hi = i_last / BN;
+  for (int base = 0; base <= jt_hi; base += 64) {
+    const int jt = base + lane;
+    unsigned need = 0, full = 0;
+    if (jt <= jt_hi) {
+      for (int w = 0; w < 4; ++w)
+        for (int rb = 0; rb < RB_MAX; ++rb) {
+          const int rlo = i0 + (w * RB_MAX + rb) * 16;
+          if (rlo > i_last) continue;
+          const int rhi = rlo + 15 < i_last ? rlo + 15 : i_last;
+          for (int kq = 0; kq < 4; ++kq) {
+            const int jlo = jt * BN + 16 * kq;
+            const unsigned bit = 1u << (w * 8 + rb * 4 + kq);
+            if (range_has_kept(rlo, rhi, jlo, jlo + 15, P, a.mode, a.W, a.B, a.G)) need |= bit;
+            if (rhi == rlo + 15 && range_all_kept(rlo, jlo + 15, P, a.mode)) full |= bit;
+          }
+        }
+    }
+    const bool keep = need != 0;
+    const uint64_t bal = __ballot(keep);
+    if (keep) {
+      const int slot = count + __popcll(bal & ((uint64_t(1) << lane) - 1));
+      out[slot] = make_int4(jt, (int)need, (int)(full & need), 0);
+    }
+    count += __popcll(bal);
+  }
+  if (lane == 0) const_cast<int32_t*>(a.tile_count)[(int64_t)b * a.n_qt + qt] = count;
+}
+
+// ---------------------------------------------------------------- attention
+template <int HD>
+__global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
+  constexpr int RB = RB_MAX;
+  constexpr int NC = HD / 32;          // 32-wide contraction chunks of the head dim
+  constexpr int NB = HD / 16;          // 16-wide output blocks of the head dim
+  constexpr int CPR = HD / 8;          // 16-byte chunks per key row
+  constexpr int RPI = 64 / CPR;        // key rows per 1 KiB wave transfer
+  constexpr int TILE = BN * HD;        // elements of one K (or V) tile
+  constexpr int DPW = BN * CPR / 256;  // 1 KiB transfers per wave per tile, K (same for V)
+  constexpr int NS = 3;                // LDS ring stages (two tiles in flight)
+
+  // ring of NS stages, each a K tile then a V tile, row-major, 16-byte
+  // chunk p of row r holding the row's chunk p ^ (r % CPR) (bank spreading)
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * 2 * TILE];
 
   const int t = threadIdx.x;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches
   const int lane = t & 63;
-  const int lr = lane & 15;          // row (or column) within a 16-block
-  const int lg = lane >> 4;          // lane group 0..3
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
 
   const int n_bh = a.batch * a.heads;
-  const int bh = blockIdx.x % n_bh;  // all query tiles of (b, h) on one XCD
+  const int bh = blockIdx.x % n_bh;    // all query tiles of (b, h) on one XCD
   const int qt = blockIdx.x / n_bh;
   const int b = bh / a.heads;
   const int h = bh % a.heads;
   const int hk = h / (a.heads / a.kv_heads);
-  const int i0 = qt * BM;
+  const int i0 = qt * BM_ROWS;
   const int n = a.n;
   const int P = clampi(a.prompt_len[b], 0, n);
-  const int i_last = i0 + BM - 1 < n - 1 ? i0 + BM - 1 : n - 1;
+  const int i_last = i0 + BM_ROWS - 1 < n - 1 ? i0 + BM_ROWS - 1 : n - 1;
+  const int mode = a.mode, W = a.W, Bw = a.B, G = a.G;
+  const bool all_residues = 2 * Bw + 1 >= G;
+  const int jt_max = (n - 1) / BN;
+
+  const int64_t lid = (int64_t)b * a.n_qt + qt;
+  const int cnt = clampi(a.tile_count[lid], 0, a.max_tiles);
+  const int4* list = a.tile_list + lid * a.max_tiles;
 
   const uint16_t* qb = a.q + b * a.sq[0] + h * a.sq[1];
   const uint16_t* kb = a.k + b * a.sk[0] + hk * a.sk[1];
   const uint16_t* vb = a.v + b * a.sv[0] + hk * a.sv[1];
 
-  // ---- this wave's query rows: 16*RB, lane lr of block rb holds row
-  // wi0 + 16*rb + lr; Q^T operand chunks kept in registers
+  // DMA of key tile jt into ring stage st: this wave's DPW transfers of K
+  // and of V; lane l of transfer u fills LDS chunk l of its 1 KiB block
+  auto issue = [&](int jt, int st) {
+    jt = clampi(jt, 0, jt_max);
+    uint16_t* kd = ring + st * 2 * TILE;
+    uint16_t* vd = kd + TILE;
+#pragma unroll
+    for (int u = 0; u < DPW; ++u) {
+      const int blk = wave * DPW + u;                 // 1 KiB block of the tile
+      const int row = blk * RPI + lane / CPR;
+      const int pos = lane % CPR;
+      const int chunk = pos ^ (row % CPR);
+      int j = jt * BN + row;
+      j = j < n ? j : n - 1;                          // rows past the end: masked later
+      __builtin_amdgcn_global_load_lds(kb + (int64_t)j * a.sk[2] + chunk * 8, kd + blk * 512, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + (int64_t)j * a.sv[2] + chunk * 8, vd + blk * 512, 16, 0, 0);
+    }
+  };
+
+  // prologue: the first NS-1 listed tiles go in flight before Q is read
+#pragma unroll
+  for (int k = 0; k < NS - 1; ++k)
+    if (k < cnt) issue(list[k].x, k);
+
+  // ---- this wave's 16*RB query rows; lane lr of block rb holds row
+  // wi0 + 16*rb + lr; its Q^T operand chunks stay in registers
   const int wi0 = i0 + wave * 16 * RB;
   bf16x8 qv[RB][NC];
 #pragma unroll
@@ -123,144 +220,153 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
       qv[rb][c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + lg * 8);
   }
 
-  float m[RB], ls[RB];
+  float mq[RB], ls[RB];                // running reference max (scaled), partial sum
   f32x4 o[RB][NB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    m[rb] = -INFINITY;
+    mq[rb] = -INFINITY;
     ls[rb] = 0.f;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // ---- kept key tiles of this query tile, in order
-  const int jt_hi = i_last / BN;
-  auto next_tile = [&](int jt) {
-    for (++jt; jt <= jt_hi; ++jt)
-      if (range_has_kept(i0, i_last, jt * BN, jt * BN + BN - 1, P, a.mode, a.W, a.B, a.G)) break;
-    return jt;
-  };
+  // transpose-read address parts of this lane (see the V^T product below)
+  const int vt_row = 4 * lg + (lr >> 2);
+  const int vt_sub = (lr & 3);
 
-  // global -> registers for one tile: thread t moves LPT 16-byte chunks of K
-  // and of V; rows past the sequence end re-read row n-1 (masked later)
-  u32x4 pk[LPT], pv[LPT];
-  auto fetch = [&](int jt) {
+  int stage = 0;
+  for (int idx = 0; idx < cnt; ++idx) {
+    // tile idx landed (at most the DMAs of tile idx+1 may remain; the first
+    // pass also waits for the Q loads)
+    if (idx == 0 || idx + 1 >= cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DPW));
+    __builtin_amdgcn_s_barrier();      // every wave's part of the tile is in LDS, and
+                                       // every wave is done with the stage refilled next
+    if (idx + NS - 1 < cnt) issue(list[idx + NS - 1].x, (stage + NS - 1) % NS);
+
+    const int4 ent = list[idx];
+    const int j0 = clampi(ent.x, 0, jt_max) * BN;
+    const unsigned needw = ((unsigned)ent.y >> (wave * 8)) & 0xffu;
+    const unsigned fullw = ((unsigned)ent.z >> (wave * 8)) & 0xffu;
+    const uint16_t* ksm = ring + stage * 2 * TILE;
+    const uint16_t* vsm = ksm + TILE;
+
+    // ---- S^T = K Q^T per 16-key block (A = K from LDS, shared by the RB
+    // row blocks)
+    f32x4 sc[RB][4];
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int idx = u * 256 + t;
-      const int kr = idx / CPR, ch = idx % CPR;
-      int j = jt * BN + kr;
-      j = j < n ? j : n - 1;
-      pk[u] = *reinterpret_cast<const u32x4*>(kb + (int64_t)j * a.sk[2] + ch * 8);
-      pv[u] = *reinterpret_cast<const u32x4*>(vb + (int64_t)j * a.sv[2] + ch * 8);
-    }
-  };
-  auto stage = [&]() {
+    for (int kq = 0; kq < 4; ++kq) {
 #pragma unroll
-    for (int u = 0; u < LPT; ++u) {
-      const int idx = u * 256 + t;
-      const int kr = idx / CPR, ch = idx % CPR;
-      *reinterpret_cast<u32x4*>(ks + kr * KSTR + ch * 8) = pk[u];
+      for (int rb = 0; rb < RB; ++rb) sc[rb][kq] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!(needw & (0x11u << kq))) continue;
+      const int row = 16 * kq + lr;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = pv[u][e];
-        vt[(ch * 8 + 2 * e) * VSTR + kr] = (uint16_t)(w & 0xffffu);
-        vt[(ch * 8 + 2 * e + 1) * VSTR + kr] = (uint16_t)(w >> 16);
+      for (int c = 0; c < NC; ++c) {
+        const int pos = (4 * c + lg) ^ (row % CPR);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ksm + row * HD + pos * 8);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (needw & (1u << (rb * 4 + kq)))
+            sc[rb][kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][kq], 0, 0, 0);
       }
     }
-  };
 
-  int jt = next_tile(-1);
-  if (jt <= jt_hi) fetch(jt);
-  while (jt <= jt_hi) {
-    __syncthreads();                 // every wave is done with the previous tile
-    stage();
-    __syncthreads();
-    const int jn = next_tile(jt);
-    if (jn <= jt_hi) fetch(jn);      // in flight while this tile computes
-    const int j0 = jt * BN;
-
+    // ---- masks, online softmax, P^T operands
+    bf16x8 pb[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const int rlo = wi0 + 16 * rb;
-      const int rhi = rlo + 15 < i_last ? rlo + 15 : i_last;
-      if (rlo > i_last) continue;
-      const int i = rlo + lr;        // this lane's row
-      // ---- S^T blocks (16 keys each), scaled to the log2 domain
-      f32x4 s[4];
-      bool need[4];
+      const int i = wi0 + 16 * rb + lr;
 #pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4) {
-        const int jlo = j0 + 16 * kb4;
-        need[kb4] = range_has_kept(rlo, rhi, jlo, jlo + 15, P, a.mode, a.W, a.B, a.G);
-        s[kb4] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (need[kb4]) {
+      for (int kq = 0; kq < 4; ++kq) {
+        const unsigned bit = 1u << (rb * 4 + kq);
+        if (!(needw & bit)) {
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ks + (16 * kb4 + lr) * KSTR + 32 * c + lg * 8);
-            s[kb4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], s[kb4], 0, 0, 0);
-          }
-          const bool full = range_all_kept(rlo, jlo + 15, P, a.mode);
+          for (int r = 0; r < 4; ++r) sc[rb][kq][r] = -INFINITY;
+        } else if (!(fullw & bit)) {
+          // element r is key jb + r at distance d0 - r
+          const int jb = j0 + 16 * kq + 4 * lg;
+          const int d0 = i - jb;
+          const int tm = (mode == DA_MODE_ROWDIAG && !all_residues) ? mod_g(d0 + Bw, G, a.inv_g) : 0;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int j = jlo + 4 * lg + r;
-            const bool kp = full || (i < n && keep_pair(i, j, P, a.mode, a.W, a.B, a.G));
-            s[kb4][r] = kp ? s[kb4][r] * a.qscale : -INFINITY;
+            const int d = d0 - r;
+            bool kp = i < n && d >= 0;
+            if (mode != DA_MODE_DENSE && jb + r >= P) {
+              bool wk = d <= W;
+              if (mode == DA_MODE_BAND) wk = wk && d <= Bw;
+              else if (!all_residues) {
+                const int tr = tm - r < 0 ? tm - r + G : tm - r;   // (d + B) mod G
+                wk = wk && tr <= 2 * Bw;
+              }
+              kp = kp && wk;
+            }
+            if (!kp) sc[rb][kq][r] = -INFINITY;
           }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) s[kb4][r] = -INFINITY;
         }
       }
-      // ---- online softmax for this lane's row
       float mt = -INFINITY;
 #pragma unroll
-      for (int kb4 = 0; kb4 < 4; ++kb4)
+      for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[kb4][r]);
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[rb][kq][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m[rb], mt);
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      const float alpha = exp2f(m[rb] - mref);
-      m[rb] = mn;
-      ls[rb] *= alpha;
+      const float mts = mt * a.qscale;
+      // lazy rescale: the reference max only moves when a row's max grows by
+      // more than 2^8 (p <= 256 stays exact enough in bf16 and fp32); the
+      // branch is taken by the whole wave or not at all
+      if (__any(mts > mq[rb] + 8.f)) {
+        const float mn = fmaxf(mq[rb], mts);
+        const float alpha = mn == -INFINITY ? 1.f : exp2f(mq[rb] - mn);
+        ls[rb] *= alpha;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[rb][nb][r] *= alpha;
-      // P^T as the B operand of O^T += V^T P^T: slot e of 32-key chunk cc is
-      // key 32cc + (e/4)*16 + 4*lg + e%4, i.e. block 2cc+e/4, element e%4
-      bf16x8 pb[2];
+          for (int r = 0; r < 4; ++r) o[rb][nb][r] *= alpha;
+        mq[rb] = mn;
+      }
+      const float mref = mq[rb] == -INFINITY ? 0.f : mq[rb];
+      // P^T as the B operand: slot e of 32-key chunk cc is key
+      // 32cc + (e/4)*16 + 4lg + e%4 = block 2cc + e/4, element e%4
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        uint16_t tmp[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(s[2 * cc + e / 4][e % 4] - mref);
+          const float p = exp2f(fmaf(sc[rb][2 * cc + e / 4][e % 4], a.qscale, -mref));
           ls[rb] += p;
-          tmp[e] = (uint16_t)f32_to_bf16(p);
-        }
-        __builtin_memcpy(&pb[cc], tmp, 16);
-      }
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        if (!need[2 * cc] && !need[2 * cc + 1]) continue;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const uint16_t* vrow = vt + (16 * nb + lr) * VSTR + 32 * cc + 4 * lg;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);        // 8-byte aligned
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-          const u32x4 w = u32x4{lo.x, lo.y, hi.x, hi.y};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
-          o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[cc], o[rb][nb], 0, 0, 0);
+          pb[rb][cc][e] = (__bf16)p;
         }
       }
     }
-    jt = jn;
+
+    // ---- O^T += V^T P^T: A = V^T by transpose reads of row-major V; lane L
+    // of group g addresses key 4g + L/4 of a 16-key half, dims
+    // 16nb + 4(L%4) .. +4, and receives keys 4g + 0..3 at dim 16nb + L
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      if (!(needw & (0x33u << (2 * cc)))) continue;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        const int chunk = 2 * nb + (vt_sub >> 1);
+        const int r_lo = 32 * cc + vt_row, r_hi = r_lo + 16;
+        const uint16_t* plo = vsm + r_lo * HD + ((chunk ^ (r_lo % CPR)) * 8) + (vt_sub & 1) * 4;
+        const uint16_t* phi = vsm + r_hi * HD + ((chunk ^ (r_hi % CPR)) * 8) + (vt_sub & 1) * 4;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          if (needw & (0x3u << (rb * 4 + 2 * cc)))
+            o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][cc], o[rb][nb], 0, 0, 0);
+      }
+    }
+    stage = (stage + 1) % NS;
   }
 
-  // ---- normalise and store: lane holds row rlo+lr, dims 16nb + 4lg + r
+  // ---- normalise and store: lane holds row wi0+16rb+lr, dims 16nb + 4lg + r
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float L = ls[rb];
@@ -277,7 +383,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<uint2*>(orow + 16 * nb + 4 * lg) = make_uint2(w0, w1);
     }
     if (a.lse && lg == 0)
-      a.lse[((int64_t)b * a.heads + h) * n + i] = (m[rb] + log2f(L)) * kLn2P;
+      a.lse[((int64_t)b * a.heads + h) * n + i] = (mq[rb] + log2f(L)) * kLn2P;
   }
 }
 
@@ -285,11 +391,60 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
 
 using namespace da;
 
+static int n_query_tiles(int n) { return (n + BM_ROWS - 1) / BM_ROWS; }
+static int max_key_tiles(int n) { return (n + BN - 1) / BN; }
+
+extern "C" int64_t da_prefill_tiles_bytes(int32_t batch, int32_t n) {
+  if (batch < 0 || n < 0) return fail(DA_EINVAL, "batch=%d n=%d", batch, n);
+  clear_error();
+  const int64_t lists = (int64_t)batch * n_query_tiles(n);
+  return ((lists * 4 + 15) / 16) * 16 + lists * max_key_tiles(n) * 16;
+}
+
+static void fill_common(PrefillArgs& a, const da_mask* m, int32_t batch, int32_t n,
+                        const int32_t* prompt_len, const void* tiles) {
+  a.prompt_len = prompt_len;
+  a.batch = batch;
+  a.n = n;
+  a.mode = m->mode;
+  a.W = m->W;
+  a.B = m->B;
+  a.G = m->G;
+  a.inv_g = 1.f / (float)m->G;
+  a.n_qt = n_query_tiles(n);
+  a.max_tiles = max_key_tiles(n);
+  const int64_t lists = (int64_t)batch * a.n_qt;
+  a.tile_count = reinterpret_cast<const int32_t*>(tiles);
+  a.tile_list = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(tiles) +
+                                              ((lists * 4 + 15) / 16) * 16);
+}
+
+extern "C" int da_prefill_tiles_build(const da_mask* m, int32_t batch, int32_t n,
+                                      const int32_t* prompt_len, void* tiles, int64_t tiles_bytes,
+                                      void* stream) {
+  int rc = check_mask(m);
+  if (rc) return rc;
+  if (!m->causal) return fail(DA_ENOTSUP, "prefill needs a causal mask");
+  if (batch < 0 || n < 0) return fail(DA_EINVAL, "batch=%d n=%d", batch, n);
+  const int64_t need = da_prefill_tiles_bytes(batch, n);
+  if (batch > 0 && n > 0 && (!prompt_len || !tiles))
+    return fail(DA_EINVAL, "prompt_len and tiles must be non-NULL");
+  if (tiles_bytes < need) return fail(DA_ECAPACITY, "tiles buffer %lld bytes < %lld", (long long)tiles_bytes, (long long)need);
+  if ((uintptr_t)tiles % 16) return fail(DA_EINVAL, "tiles buffer not 16-byte aligned");
+  clear_error();
+  if (batch == 0 || n == 0) return DA_OK;
+  PrefillArgs a{};
+  fill_common(a, m, batch, n, prompt_len, tiles);
+  const int64_t blocks = (int64_t)batch * a.n_qt;
+  hipLaunchKernelGGL(prefill_tiles_kernel, dim3((unsigned)blocks), dim3(64), 0, (hipStream_t)stream, a);
+  return check_launch("prefill_tiles_kernel");
+}
+
 extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t batch, int32_t heads,
                                     int32_t kv_heads, int32_t n, int32_t head_dim,
                                     const void* q, const void* k, const void* v, void* out,
                                     const int64_t* strides, const int32_t* prompt_len,
-                                    float scale, float* lse, void* stream) {
+                                    const void* tiles, float scale, float* lse, void* stream) {
   int rc = check_mask(m);
   if (rc) return rc;
   if (!m->causal) return fail(DA_ENOTSUP, "prefill needs a causal mask");
@@ -298,15 +453,15 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
   if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads || n < 0)
     return fail(DA_EINVAL, "batch=%d heads=%d kv_heads=%d n=%d", batch, heads, kv_heads, n);
   if (!strides) return fail(DA_EINVAL, "strides is NULL");
-  if (batch > 0 && n > 0 && (!q || !k || !v || !out || !prompt_len))
-    return fail(DA_EINVAL, "q, k, v, out and prompt_len must be non-NULL");
+  if (batch > 0 && n > 0 && (!q || !k || !v || !out || !prompt_len || !tiles))
+    return fail(DA_EINVAL, "q, k, v, out, prompt_len and tiles must be non-NULL");
   for (int i = 0; i < 12; ++i)
     if (strides[i] < 0 || (strides[i] * 2) % 16) return fail(DA_EINVAL, "stride %d must be a non-negative multiple of 8 elements", i);
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16)
-    return fail(DA_EINVAL, "q, k, v and out must be 16-byte aligned");
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)tiles) % 16)
+    return fail(DA_EINVAL, "q, k, v, out and tiles must be 16-byte aligned");
   clear_error();
   if (batch == 0 || n == 0) return DA_OK;
-  PrefillArgs a;
+  PrefillArgs a{};
   a.q = reinterpret_cast<const uint16_t*>(q);
   a.k = reinterpret_cast<const uint16_t*>(k);
   a.v = reinterpret_cast<const uint16_t*>(v);
@@ -318,24 +473,15 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
     a.sv[i] = strides[6 + i];
     a.so[i] = strides[9 + i];
   }
-  a.prompt_len = prompt_len;
-  a.batch = batch;
+  fill_common(a, m, batch, n, prompt_len, tiles);
   a.heads = heads;
   a.kv_heads = kv_heads;
-  a.n = n;
-  a.mode = m->mode;
-  a.W = m->W;
-  a.B = m->B;
-  a.G = m->G;
   a.qscale = scale * kLog2eP;
-  constexpr int RB = 1;
-  const int bm = 64 * RB;
-  a.n_qt = (n + bm - 1) / bm;
   const int64_t blocks = (int64_t)a.n_qt * batch * heads;
   if (blocks > 0x7fffffff) return fail(DA_ENOTSUP, "grid too large");
   if (head_dim == 128)
-    hipLaunchKernelGGL((prefill_kernel<128, RB>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<64, RB>), dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
   return check_launch("prefill_kernel");
 }

@@ -172,6 +172,94 @@ class DecodeBench:
         return (time.perf_counter() - t0) * 1e6 / steps
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16, AMD public spec
+
+
+class PrefillBench:
+    """The band-masked prefill workload on the device, with rotation copies
+    so that each timed launch reads Q, K, V cold from HBM."""
+
+    def __init__(self, cfg, n_copies=4):
+        import torch
+        import ar_image_generation_amd as da
+        import workloads as wl
+        self.torch, self.da, self.cfg = torch, da, cfg
+        t0 = time.time()
+        inp = wl.prefill_inputs(cfg)
+        dev = torch.device("cuda:0")
+        self.q = [inp.q.to(dev)]
+        self.k = [inp.k.to(dev)]
+        self.v = [inp.v.to(dev)]
+        for _ in range(n_copies - 1):
+            self.q.append(self.q[0].clone())
+            self.k.append(self.k[0].clone())
+            self.v.append(self.v[0].clone())
+        self.o = [torch.empty_like(self.q[0]) for _ in range(n_copies)]
+        self.prompt = inp.prompt_len.to(dev)
+        self.tiles = {md: da.prefill_tiles_build(da.mask(md, cfg.W, cfg.B, cfg.G), self.prompt, cfg.n)
+                      for md in (cfg.mode, da.DENSE)}
+        self.n_copies = n_copies
+        self.bytes = 4 * self.q[0].numel() * 2          # Q, K, V read once, O written once
+        per_head = {}
+        for mode in (cfg.mode, da.DENSE):
+            m = da.mask(mode, cfg.W, cfg.B, cfg.G)
+            per_head[mode] = sum(da.keep_count(m, i, cfg.P) for i in range(cfg.n))
+        self.kept_pairs = {md: c * cfg.batch * cfg.heads for md, c in per_head.items()}
+        torch.cuda.synchronize()
+        log(f"[bench] {cfg.name}: inputs + {n_copies} copies in {time.time() - t0:.1f}s, "
+            f"kept pairs/head {per_head[cfg.mode]} (dense causal {per_head[da.DENSE]})")
+
+    def run(self, mode, c):
+        cfg = self.cfg
+        self.da.band_prefill_attn(self.da.mask(mode, cfg.W, cfg.B, cfg.G), self.q[c], self.k[c],
+                                  self.v[c], self.prompt, tiles=self.tiles[mode], out=self.o[c])
+
+    def time_graph(self, mode, steps, warmup):
+        torch = self.torch
+        for w in range(warmup):
+            self.run(mode, w % self.n_copies)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for s in range(steps):
+                self.run(mode, s % self.n_copies)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / steps
+
+    def report(self, steps, warmup):
+        cfg, da = self.cfg, self.da
+        us = self.time_graph(cfg.mode, steps, warmup)
+        us_d = self.time_graph(da.DENSE, max(4, steps // 2), warmup)
+        flops = 4.0 * cfg.hd * self.kept_pairs[cfg.mode]
+        flops_d = 4.0 * cfg.hd * self.kept_pairs[da.DENSE]
+        hbm_floor = self.bytes / (HBM_PEAK_GBPS * 1e3)            # us
+        mfma_floor = flops / (MFMA_BF16_PEAK_TFLOPS * 1e6)       # us
+        rec = {
+            "workload": cfg.name, "us": round(us, 2),
+            "bytes_MB": round(self.bytes / 1e6, 2), "kept_pairs": self.kept_pairs[cfg.mode],
+            "algorithmic_GFLOP": round(flops / 1e9, 3),
+            "achieved_GBps": round(self.bytes / (us * 1e-6) / 1e9, 1),
+            "achieved_TFLOPs": round(flops / (us * 1e-6) / 1e12, 2),
+            "hbm_floor_us": round(hbm_floor, 2), "mfma_floor_us": round(mfma_floor, 2),
+            "bound": "hbm" if hbm_floor >= mfma_floor else "mfma",
+            "roofline_frac": round(max(hbm_floor, mfma_floor) / us, 4),
+            "dense_causal_us": round(us_d, 2),
+            "dense_causal_TFLOPs": round(flops_d / (us_d * 1e-6) / 1e12, 2),
+            "speedup_vs_dense": round(us_d / us, 3),
+        }
+        log(f"[bench] {cfg.name}: {us:.2f} us ({rec['achieved_TFLOPs']} TFLOP/s, "
+            f"{rec['achieved_GBps']} GB/s), dense causal {us_d:.2f} us")
+        return rec
+
+
 def cpu_baseline(cfg, budget_s=12.0):
     """The oracle, as it stands, on the same workload: all queries of the
     batch, repeated until about `budget_s` seconds of CPU work."""
@@ -412,6 +500,13 @@ def main():
             del eb
             torch.cuda.empty_cache()
 
+    prefill = None
+    if not args.no_extra:
+        pb = PrefillBench(wl.PREFILL_CONFIGS["prefill_b2"])
+        prefill = pb.report(max(8, K // 4), 2)
+        del pb
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle ...")
@@ -449,6 +544,7 @@ def main():
                   "speedup_step": round(us_step_d / us_step, 3),
                   "speedup_decode": round(us_dec_d / us_dec, 3)},
         "extra": extra,
+        "prefill": prefill,
     }
     print(json.dumps(line), flush=True)
 

@@ -185,6 +185,29 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
                           int32_t split, void* out, float* lse,
                           void* workspace, int64_t ws_bytes, void* stream);
 
+/* [host] Bytes of the prefill tile lists for `batch` sequences of n tokens. */
+int64_t da_prefill_tiles_bytes(int32_t batch, int32_t n);
+
+/* prefill_tiles_build -- the tile lists of the keep-set for prefill.
+ *
+ * Queries are cut into tiles of 128 rows (4 waves x 2 blocks of 16) and keys
+ * into tiles of 64 (4 blocks of 16).  For each batch b and query tile qt
+ * this writes, in key order, the key tiles that hold at least one kept
+ * (row, key) pair of the causal keep rule (prompt_len[b] prompt tokens), and
+ * for each two 32-bit masks over (wave w, row block rb, key block kq), bit
+ * w*8 + rb*4 + kq: the block holds a kept pair / every pair of the block is
+ * kept.  Layout of `tiles` (16-byte aligned, da_prefill_tiles_bytes long):
+ *   int32 count[batch][n_qt], padded to 16 bytes, then
+ *   int32 entry[batch][n_qt][max_tiles][4] = {key tile, need mask, full mask, 0}
+ * with n_qt = ceil(n / 128), max_tiles = ceil(n / 64).  The lists depend only
+ * on the mask, n and prompt_len: build them once and reuse them for every
+ * head and layer.
+ * Errors: DA_EINVAL (mask, sizes, null pointers, alignment), DA_ENOTSUP
+ * (causal = 0), DA_ECAPACITY (tiles_bytes too small). */
+int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t n,
+                           const int32_t* prompt_len, void* tiles, int64_t tiles_bytes,
+                           void* stream);
+
 /* band_prefill_attn -- keep-set-masked causal attention over whole sequences
  * (prefill), on the matrix cores.
  *
@@ -195,7 +218,10 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
  * prompt tokens, hk = h / (heads / kv_heads).  This is the summary's masked
  * softmax (core formulas) applied to every row of the sequence; the pages
  * apply the sparsity to decode, and this call serves the same mask where a
- * whole sequence is attended at once.
+ * whole sequence is attended at once.  Only the key tiles and 16x16 blocks
+ * listed in `tiles` (da_prefill_tiles_build with the same mask, n and
+ * prompt_len) are computed; element masks are applied inside blocks that
+ * are not entirely kept.
  *
  *   q, out [batch][heads][n][head_dim], k, v [batch][kv_heads][n][head_dim],
  *          bf16, head_dim elements contiguous and 16-byte aligned;
@@ -204,14 +230,16 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
  *   prompt_len [batch] (device; read clamped to [0, n]);
  *   lse [batch][heads][n] fp32 natural-log sums, or NULL.
  * Scores accumulate in fp32 from bf16 products; probabilities are rounded to
- * bf16 for the second product; outputs round to nearest even.
+ * bf16 for the second product; outputs round to nearest even.  Tile entries
+ * and counts are clamped into range, so an inconsistent list gives wrong
+ * numbers, never an out-of-bounds access.
  * Errors: DA_EINVAL (mask, null pointers, sizes, strides, alignment),
  * DA_ENOTSUP (causal = 0, dtype other than bf16, head_dim not 64/128). */
 int da_band_prefill_attn(const da_mask* m /* [host] */, da_dtype dtype, int32_t batch,
                          int32_t heads, int32_t kv_heads, int32_t n, int32_t head_dim,
                          const void* q, const void* k, const void* v, void* out,
                          const int64_t* strides /* [host] 12 */, const int32_t* prompt_len,
-                         float scale, float* lse, void* stream);
+                         const void* tiles, float scale, float* lse, void* stream);
 
 /* Measurement: streaming read of `bytes` bytes at `buf` (16-byte aligned, a
  * multiple of 16) by `grid` workgroups of 256 threads, 16-byte loads, eight
