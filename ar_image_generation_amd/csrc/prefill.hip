@@ -38,16 +38,19 @@ struct PrefillArgs {
   int64_t sq[3], sk[3], sv[3], so[3];   // element strides (batch, head, position)
   const int32_t* prompt_len;        // [batch]
   const int32_t* tile_count;        // [batch][n_qt]
-  const int4* tile_list;            // [batch][n_qt][max_tiles] (key tile, need bits, full bits, -)
+  const int4* tile_list;            // [batch][n_qt][max_tiles][2]: (key tile, need lo, need hi, 0),
+                                    // (full lo, full hi, 0, 0)
   int batch, heads, kv_heads, n, n_qt, max_tiles;
   int mode, W, B, G;
   float qscale;                     // scale * log2(e)
   float inv_g;                      // 1 / G
 };
 
-// Query tile: 4 waves x RB_MAX row blocks of 16 rows; key tile: BN keys.
+// Query tile: NWAVE waves x RB_MAX row blocks of 16 rows; key tile: BN keys.
 constexpr int RB_MAX = 2;
-constexpr int BM_ROWS = 64 * RB_MAX;
+constexpr int NWAVE = 8;
+constexpr int BM_ROWS = NWAVE * 16 * RB_MAX;
+constexpr int NTHREADS = NWAVE * 64;
 
 constexpr int BN = 64;              // keys per tile
 constexpr float kLog2eP = 1.4426950408889634f;
@@ -97,7 +100,7 @@ __device__ inline int mod_g(int x, int G, float inv_g) {
 
 // ---------------------------------------------------------------- tile lists
 // For query tile qt of batch b: the key tiles (BN keys) holding a kept pair,
-// in order, each with two 32-bit masks over (wave, row block, 16-key block)
+// in order, each with two 64-bit masks over (wave, row block, 16-key block)
 // -- bit w*8 + rb*4 + kq: that block has a kept pair / every pair is kept.
 // One wave per (b, qt); lane = candidate key tile; a ballot keeps the order.
 __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
@@ -108,21 +111,21 @@ __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
   const int P = clampi(a.prompt_len[b], 0, n);
   const int i0 = qt * BM_ROWS;
   const int i_last = i0 + BM_ROWS - 1 < n - 1 ? i0 + BM_ROWS - 1 : n - 1;
-  int4* out = const_cast<int4*>(a.tile_list) + ((int64_t)b * a.n_qt + qt) * a.max_tiles;
+  int4* out = const_cast<int4*>(a.tile_list) + ((int64_t)b * a.n_qt + qt) * a.max_tiles * 2;
   int count = 0;
   const int jt_hi = i_last / BN;
   for (int base = 0; base <= jt_hi; base += 64) {
     const int jt = base + lane;
-    unsigned need = 0, full = 0;
+    uint64_t need = 0, full = 0;
     if (jt <= jt_hi) {
-      for (int w = 0; w < 4; ++w)
+      for (int w = 0; w < NWAVE; ++w)
         for (int rb = 0; rb < RB_MAX; ++rb) {
           const int rlo = i0 + (w * RB_MAX + rb) * 16;
           if (rlo > i_last) continue;
           const int rhi = rlo + 15 < i_last ? rlo + 15 : i_last;
           for (int kq = 0; kq < 4; ++kq) {
             const int jlo = jt * BN + 16 * kq;
-            const unsigned bit = 1u << (w * 8 + rb * 4 + kq);
+            const uint64_t bit = uint64_t(1) << (w * 8 + rb * 4 + kq);
             if (range_has_kept(rlo, rhi, jlo, jlo + 15, P, a.mode, a.W, a.B, a.G)) need |= bit;
             if (rhi == rlo + 15 && range_all_kept(rlo, jlo + 15, P, a.mode)) full |= bit;
           }
@@ -132,7 +135,9 @@ __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
     const uint64_t bal = __ballot(keep);
     if (keep) {
       const int slot = count + __popcll(bal & ((uint64_t(1) << lane) - 1));
-      out[slot] = make_int4(jt, (int)need, (int)(full & need), 0);
+      full &= need;
+      out[2 * slot] = make_int4(jt, (int)(uint32_t)need, (int)(uint32_t)(need >> 32), 0);
+      out[2 * slot + 1] = make_int4((int)(uint32_t)full, (int)(uint32_t)(full >> 32), 0, 0);
     }
     count += __popcll(bal);
   }
@@ -141,15 +146,15 @@ __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
 
 // ---------------------------------------------------------------- attention
 template <int HD>
-__global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   constexpr int RB = RB_MAX;
   constexpr int NC = HD / 32;          // 32-wide contraction chunks of the head dim
   constexpr int NB = HD / 16;          // 16-wide output blocks of the head dim
   constexpr int CPR = HD / 8;          // 16-byte chunks per key row
   constexpr int RPI = 64 / CPR;        // key rows per 1 KiB wave transfer
   constexpr int TILE = BN * HD;        // elements of one K (or V) tile
-  constexpr int DPW = BN * CPR / 256;  // 1 KiB transfers per wave per tile, K (same for V)
-  constexpr int NS = 3;                // LDS ring stages (two tiles in flight)
+  constexpr int DPW = BN * CPR / NTHREADS;  // 1 KiB transfers per wave per tile, K (same for V)
+  constexpr int NS = 4;                // LDS ring stages (see the loop below)
 
   // ring of NS stages, each a K tile then a V tile, row-major, 16-byte
   // chunk p of row r holding the row's chunk p ^ (r % CPR) (bank spreading)
@@ -177,7 +182,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
 
   const int64_t lid = (int64_t)b * a.n_qt + qt;
   const int cnt = clampi(a.tile_count[lid], 0, a.max_tiles);
-  const int4* list = a.tile_list + lid * a.max_tiles;
+  const int4* list = a.tile_list + lid * a.max_tiles * 2;
 
   const uint16_t* qb = a.q + b * a.sq[0] + h * a.sq[1];
   const uint16_t* kb = a.k + b * a.sk[0] + hk * a.sk[1];
@@ -202,10 +207,9 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // prologue: the first NS-1 listed tiles go in flight before Q is read
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k)
-    if (k < cnt) issue(list[k].x, k);
+    if (k < cnt) issue(list[2 * k].x, k);
 
   // ---- this wave's 16*RB query rows; lane lr of block rb holds row
   // wi0 + 16*rb + lr; its Q^T operand chunks stay in registers
@@ -230,35 +234,17 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     for (int nb = 0; nb < NB; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // transpose-read address parts of this lane (see the V^T product below)
   const int vt_row = 4 * lg + (lr >> 2);
   const int vt_sub = (lr & 3);
+  const int my_i0 = wi0 + lr;          // this lane's row in block 0 (block rb adds 16 rb)
 
-  int stage = 0;
-  for (int idx = 0; idx < cnt; ++idx) {
-    // tile idx landed (at most the DMAs of tile idx+1 may remain; the first
-    // pass also waits for the Q loads)
-    if (idx == 0 || idx + 1 >= cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DPW));
-    __builtin_amdgcn_s_barrier();      // every wave's part of the tile is in LDS, and
-                                       // every wave is done with the stage refilled next
-    if (idx + NS - 1 < cnt) issue(list[idx + NS - 1].x, (stage + NS - 1) % NS);
-
-    const int4 ent = list[idx];
-    const int j0 = clampi(ent.x, 0, jt_max) * BN;
-    const unsigned needw = ((unsigned)ent.y >> (wave * 8)) & 0xffu;
-    const unsigned fullw = ((unsigned)ent.z >> (wave * 8)) & 0xffu;
-    const uint16_t* ksm = ring + stage * 2 * TILE;
-    const uint16_t* vsm = ksm + TILE;
-
-    // ---- S^T = K Q^T per 16-key block (A = K from LDS, shared by the RB
-    // row blocks)
-    f32x4 sc[RB][4];
+  // S^T = K Q^T for every 16-key block of one staged tile (A = K from LDS,
+  // shared by the RB row blocks)
+  auto scores = [&](const uint16_t* ksm, f32x4 (&sc)[RB][4]) {
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) sc[rb][kq] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (!(needw & (0x11u << kq))) continue;
       const int row = 16 * kq + lr;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -266,25 +252,54 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ksm + row * HD + pos * 8);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          if (needw & (1u << (rb * 4 + kq)))
-            sc[rb][kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][kq], 0, 0, 0);
+          sc[rb][kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][kq], 0, 0, 0);
       }
     }
+  };
 
-    // ---- masks, online softmax, P^T operands
-    bf16x8 pb[RB][2];
+  // Software pipeline over the listed tiles.  Iteration idx computes the
+  // scores of tile idx+1 while it runs the softmax and P.V of tile idx, so
+  // the matrix cores and the vector ALUs work at the same time.  Stages:
+  // tile t lives in stage t % NS; at the top of iteration idx tile idx+1
+  // must have landed (tile idx+2 may still be in flight) and everyone must
+  // be done with iteration idx-1, whose stage receives tile idx+3.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_barrier();
+  f32x4 sc_cur[RB][4];
+  scores(ring, sc_cur);
+  for (int idx = 0; idx < cnt; ++idx) {
+    if (idx + 2 < cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DPW));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    if (idx + NS - 1 < cnt) issue(list[2 * (idx + NS - 1)].x, (idx + NS - 1) % NS);
+
+    const int4 e0 = list[2 * idx];
+    const int4 e1 = list[2 * idx + 1];
+    const uint64_t need64 = (uint64_t)(uint32_t)e0.y | ((uint64_t)(uint32_t)e0.z << 32);
+    const uint64_t full64 = (uint64_t)(uint32_t)e1.x | ((uint64_t)(uint32_t)e1.y << 32);
+    const unsigned needw = (unsigned)(need64 >> (wave * 8)) & 0xffu;
+    const unsigned fullw = (unsigned)(full64 >> (wave * 8)) & 0xffu;
+    const int j0 = clampi(e0.x, 0, jt_max) * BN;
+    const uint16_t* vsm = ring + (idx % NS) * 2 * TILE + TILE;
+
+    // scores of the next tile (its stage is resident; past the end this
+    // reads a stale stage and the result is never used)
+    f32x4 sc_nxt[RB][4];
+    const uint16_t* knext = ring + ((idx + 1) % NS) * 2 * TILE;
+
+    scores(knext, sc_nxt);
+
+    // ---- masks of tile idx: empty blocks -> -inf, partial blocks -> rule
+    if (fullw != 0xffu) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int i = wi0 + 16 * rb + lr;
+      for (int rb = 0; rb < RB; ++rb) {
+        const int i = my_i0 + 16 * rb;
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq) {
-        const unsigned bit = 1u << (rb * 4 + kq);
-        if (!(needw & bit)) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[rb][kq][r] = -INFINITY;
-        } else if (!(fullw & bit)) {
-          // element r is key jb + r at distance d0 - r
-          const int jb = j0 + 16 * kq + 4 * lg;
+        for (int kq = 0; kq < 4; ++kq) {
+          const unsigned bit = 1u << (rb * 4 + kq);
+          const bool empty = !(needw & bit);
+          const bool partial = !empty && !(fullw & bit);
+          const int jb = j0 + 16 * kq + 4 * lg;       // element r is key jb + r
           const int d0 = i - jb;
           const int tm = (mode == DA_MODE_ROWDIAG && !all_residues) ? mod_g(d0 + Bw, G, a.inv_g) : 0;
 #pragma unroll
@@ -294,30 +309,33 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
             if (mode != DA_MODE_DENSE && jb + r >= P) {
               bool wk = d <= W;
               if (mode == DA_MODE_BAND) wk = wk && d <= Bw;
-              else if (!all_residues) {
-                const int tr = tm - r < 0 ? tm - r + G : tm - r;   // (d + B) mod G
-                wk = wk && tr <= 2 * Bw;
-              }
+              else if (!all_residues) wk = wk && (tm - r < 0 ? tm - r + G : tm - r) <= 2 * Bw;
               kp = kp && wk;
             }
-            if (!kp) sc[rb][kq][r] = -INFINITY;
+            kp = !empty && (!partial || kp);
+            sc_cur[rb][kq][r] = kp ? sc_cur[rb][kq][r] : -INFINITY;
           }
         }
       }
+    }
+
+    // ---- online softmax (lazy reference max) and P^T operands
+    bf16x8 pb[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
       float mt = -INFINITY;
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[rb][kq][r]);
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc_cur[rb][kq][r]);
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
       const float mts = mt * a.qscale;
-      // lazy rescale: the reference max only moves when a row's max grows by
-      // more than 2^8 (p <= 256 stays exact enough in bf16 and fp32); the
-      // branch is taken by the whole wave or not at all
+      // the reference max only moves when a row's max grows by more than 2^8
+      // (p <= 256 is exact enough in bf16 and fp32); whole wave or none
       if (__any(mts > mq[rb] + 8.f)) {
         const float mn = fmaxf(mq[rb], mts);
-        const float alpha = mn == -INFINITY ? 1.f : exp2f(mq[rb] - mn);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mq[rb] - mn);
         ls[rb] *= alpha;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -326,13 +344,12 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
         mq[rb] = mn;
       }
       const float mref = mq[rb] == -INFINITY ? 0.f : mq[rb];
-      // P^T as the B operand: slot e of 32-key chunk cc is key
-      // 32cc + (e/4)*16 + 4lg + e%4 = block 2cc + e/4, element e%4
+      // slot e of 32-key chunk cc is key 32cc + (e/4)*16 + 4lg + e%4
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = exp2f(fmaf(sc[rb][2 * cc + e / 4][e % 4], a.qscale, -mref));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc_cur[rb][2 * cc + e / 4][e % 4], a.qscale, -mref));
           ls[rb] += p;
           pb[rb][cc][e] = (__bf16)p;
         }
@@ -344,7 +361,6 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
     // 16nb + 4(L%4) .. +4, and receives keys 4g + 0..3 at dim 16nb + L
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-      if (!(needw & (0x33u << (2 * cc)))) continue;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -359,11 +375,13 @@ __global__ void __launch_bounds__(256) prefill_kernel(PrefillArgs a) {
         const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          if (needw & (0x3u << (rb * 4 + 2 * cc)))
-            o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][cc], o[rb][nb], 0, 0, 0);
+          o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][cc], o[rb][nb], 0, 0, 0);
       }
     }
-    stage = (stage + 1) % NS;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq) sc_cur[rb][kq] = sc_nxt[rb][kq];
   }
 
   // ---- normalise and store: lane holds row wi0+16rb+lr, dims 16nb + 4lg + r
@@ -398,7 +416,7 @@ extern "C" int64_t da_prefill_tiles_bytes(int32_t batch, int32_t n) {
   if (batch < 0 || n < 0) return fail(DA_EINVAL, "batch=%d n=%d", batch, n);
   clear_error();
   const int64_t lists = (int64_t)batch * n_query_tiles(n);
-  return ((lists * 4 + 15) / 16) * 16 + lists * max_key_tiles(n) * 16;
+  return ((lists * 4 + 15) / 16) * 16 + lists * max_key_tiles(n) * 32;
 }
 
 static void fill_common(PrefillArgs& a, const da_mask* m, int32_t batch, int32_t n,
@@ -480,8 +498,8 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
   const int64_t blocks = (int64_t)a.n_qt * batch * heads;
   if (blocks > 0x7fffffff) return fail(DA_ENOTSUP, "grid too large");
   if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)blocks), dim3(NTHREADS), 0, (hipStream_t)stream, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, a);
+    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)blocks), dim3(NTHREADS), 0, (hipStream_t)stream, a);
   return check_launch("prefill_kernel");
 }

@@ -323,10 +323,16 @@ PROBE_BYTES = 256 << 20
 def profile_run(args):
     """Only the timed launches (for rocprofv3): K cold steps of the headline
     workload, then one streaming-read probe of PROBE_BYTES (the counter
-    calibration: a read of known size)."""
+    calibration: a read of known size).  With --prefill: K launches of the
+    band prefill instead."""
     import torch
     import workloads as wl
     import ar_image_generation_amd as da
+    if args.prefill:
+        pb = PrefillBench(wl.PREFILL_CONFIGS["prefill_b2"], n_copies=2)
+        us = pb.time_graph(pb.cfg.mode, args.steps, args.warmup)
+        log(f"[bench] prefill profile run: {us:.2f} us per launch")
+        return
     cfg = wl.CONFIGS[args.workload]
     b = DecodeBench(cfg, split=args.split)
     us = b.time_graph(cfg.modes[0], args.steps, args.warmup)
@@ -419,6 +425,74 @@ def summarize(args):
     print("\n".join(lines))
 
 
+def summarize_prefill(args):
+    """Writes profiles/prefill_<workload>.txt from rocprofv3 runs of
+    `bench.py --profile-run --prefill`: --kernel-trace, and two --pmc runs
+    (matrix-core busy cycles with GRBM_GUI_ACTIVE; instruction mix)."""
+    import csv
+    import glob
+    import workloads as wl
+    import ar_image_generation_amd as da
+    cfg = wl.PREFILL_CONFIGS["prefill_b2"]
+    trace_dir, busy_dir, mix_dir = args.summarize
+
+    def rows(d, suffix):
+        out = []
+        for f in glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True):
+            out += list(csv.DictReader(open(f)))
+        return out
+
+    tr = [r for r in rows(trace_dir, "kernel_trace.csv") if "prefill_kernel" in r["Kernel_Name"]]
+    durs = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr)
+    avg = sum(durs) / len(durs) if durs else float("nan")
+
+    def per_dispatch(d):
+        acc = {}
+        for r in rows(d, "counter_collection.csv"):
+            if "prefill_kernel" not in r["Kernel_Name"]:
+                continue
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        names = sorted({k[1] for k in acc})
+        disp = sorted({k[0] for k in acc})
+        return {nm: sum(acc[(dd, nm)] for dd in disp if (dd, nm) in acc) / max(1, len(disp))
+                for nm in names}
+
+    busy = per_dispatch(busy_dir)
+    mix = per_dispatch(mix_dir)
+    n_xcd, n_simd = 8, 1024
+    util = None
+    if busy.get("GRBM_GUI_ACTIVE") and busy.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+        cycles = busy["GRBM_GUI_ACTIVE"] / n_xcd          # per-XCD counter, summed over XCDs
+        util = busy["SQ_VALU_MFMA_BUSY_CYCLES"] / (n_simd * cycles)
+    m = da.mask(cfg.mode, cfg.W, cfg.B, cfg.G)
+    kept = sum(da.keep_count(m, i, cfg.P) for i in range(cfg.n)) * cfg.batch * cfg.heads
+    flops = 4.0 * cfg.hd * kept
+    bytes_ = 4 * cfg.batch * cfg.heads * cfg.n * cfg.hd * 2
+    lines = [
+        f"# rocprofv3 summary: band prefill kernel, workload {cfg.name}",
+        f"# (batch {cfg.batch} x {cfg.heads} heads x {cfg.n} tokens, head_dim {cfg.hd}, bf16; causal and "
+        f"prompt {cfg.P} + row-diagonal W={cfg.W} B={cfg.B} G={cfg.G})",
+        "# commands (repo root, TMPDIR=/tmp):",
+        f"#   rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o run -- python3 bench.py --profile-run --prefill --steps {args.steps} --warmup {args.warmup}",
+        f"#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -f csv -d {busy_dir} -o run -- python3 bench.py --profile-run --prefill --steps {args.steps} --warmup {args.warmup}",
+        f"#   rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_WAVES -f csv -d {mix_dir} -o run -- python3 bench.py --profile-run --prefill --steps {args.steps} --warmup {args.warmup}",
+        f"#   python3 bench.py --summarize {trace_dir} {busy_dir} {mix_dir} --prefill",
+        "# mfma_utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs)",
+        f"kernel = {tr[0]['Kernel_Name'] if tr else '?'}",
+        f"dispatches = {len(durs)}",
+        f"avg_duration_us = {avg / 1e3:.3f}",
+        f"median_duration_us = {durs[len(durs) // 2] / 1e3 if durs else float('nan'):.3f}",
+        f"algorithmic_GFLOP = {flops / 1e9:.3f}",
+        f"achieved_TFLOPs_from_avg = {flops / avg / 1e3 if durs else float('nan'):.2f}",
+        f"hbm_bytes_QKVO = {bytes_}",
+        f"mfma_utilisation = {util}",
+    ] + [f"{k} = {v:.6g}" for k, v in sorted(busy.items())] + [f"{k} = {v:.6g}" for k, v in sorted(mix.items())]
+    out = os.path.join(ROOT, "profiles", f"prefill_{cfg.name}.txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -430,11 +504,16 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
     ap.add_argument("--profile-run", action="store_true",
                     help="run only the timed decode launches and one probe (for rocprofv3)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="with --profile-run / --summarize: the band prefill kernel")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="write the profiles/ summary from three rocprofv3 output folders")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args)
+        if args.prefill:
+            summarize_prefill(args)
+        else:
+            summarize(args)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
