@@ -4,12 +4,14 @@
 // listed keys).  Each K/V row (head_dim elements, 128-512 bytes) is read by
 // LPR = row_bytes / 16 consecutive lanes with one 16-byte load each, so one
 // wave instruction moves 1 KiB and the rows of a run are contiguous in
-// memory.  A thread owns NP row slots of the chunk.  Loads are issued in
-// three phases -- every index, then (paged caches) every block-table entry,
-// then every K and V row -- so a workgroup's whole chunk (up to 128 KiB) is
-// in flight after two short dependent latencies.  The kernel is bound by HBM
-// bandwidth on the kept bytes and uses each byte once, so K/V go straight to
-// registers; LDS only carries the cross-wave softmax/output reduction.
+// memory.  Rows are taken in tiles of NP passes (NP * 256 / LPR rows); two
+// tiles are in flight while the older one is reduced.  Before the first
+// tile, every index of the chunk, then (paged caches) every block-table
+// entry, is read in one round trip each and turned into a row offset in LDS,
+// so no K/V load waits on more than the loads issued before it.  The kernel
+// is bound by HBM bandwidth on the kept bytes and uses each byte once, so
+// K/V go straight to registers; LDS only carries the row offsets and the
+// cross-wave softmax/output reduction.
 //
 // All hq/hkv query heads that share a kv head are served by the same
 // workgroup, so each kept row is read once.  Scores are q . k scaled by
@@ -414,8 +416,8 @@ typedef void (*merge_fn)(DecodeArgs);
 template <bool BF16, int HD, int GRP>
 static decode_fn pick_np(int np) {
   if (np <= 2) return decode_kernel<BF16, HD, GRP, 2>;
-  if (np <= 4) return decode_kernel<BF16, HD, GRP, 4>;
-  return decode_kernel<BF16, HD, GRP, 8>;
+  if (np == 3) return decode_kernel<BF16, HD, GRP, 3>;
+  return decode_kernel<BF16, HD, GRP, 4>;
 }
 
 template <bool BF16, int HD>
@@ -424,8 +426,26 @@ static decode_fn pick_grp(int grp, int np) {
     case 1: return pick_np<BF16, HD, 1>(np);
     case 2: return pick_np<BF16, HD, 2>(np);
     case 4: return pick_np<BF16, HD, 4>(np);
-    default: return pick_np<BF16, HD, 8>(np < 4 ? np : 4);
+    default: return pick_np<BF16, HD, 8>(np);
   }
+}
+
+// Row slots past a list's end still issue their (redundant) loads, and on
+// this part the per-CU load path is what such slots cost: the tile depth is
+// the one of 2, 3 or 4 passes that leaves the fewest empty slots for a chunk
+// of `chunk` rows, ties going to the deeper tile.
+static int tile_depth(int chunk, int rows_per_pass) {
+  int best = 4;
+  int64_t best_slots = INT64_MAX;
+  for (int np = 4; np >= 2; --np) {
+    const int64_t tile = (int64_t)np * rows_per_pass;
+    const int64_t slots = (chunk + tile - 1) / tile * tile;
+    if (slots < best_slots) {
+      best_slots = slots;
+      best = np;
+    }
+  }
+  return best;
 }
 
 // Longest chunk one workgroup takes: its row offsets live in LDS (8 B each).
@@ -520,11 +540,8 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
   a.ws_o = wl.bytes ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
   a.ws_ml = wl.bytes ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
 
-  // tile depth: the smallest NP whose two in-flight tiles cover the chunk
   const int chunk = split < cap ? split : cap;
-  const int rpp = 256 / (head_dim * esz / 16);
-  const int want = (chunk + 2 * rpp - 1) / (2 * rpp);
-  const int np = want <= 2 ? 2 : (want <= 4 ? 4 : 8);
+  const int np = tile_depth(chunk, 256 / (head_dim * esz / 16));
   decode_fn dk;
   merge_fn mk;
   if (dtype == DA_BF16) {
