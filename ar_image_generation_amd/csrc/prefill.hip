@@ -98,6 +98,19 @@ __device__ inline int mod_g(int x, int G, float inv_g) {
   return r;
 }
 
+// Bits lo..hi of a 64-bit word, clipped to 0..63; 0 when the range is empty.
+__device__ inline uint64_t bit_range(int lo, int hi) {
+  lo = lo < 0 ? 0 : lo;
+  hi = hi > 63 ? 63 : hi;
+  const int len = hi - lo;
+  const uint64_t m = (~uint64_t(0) >> (63 - (len < 0 ? 0 : len))) << (lo > 63 ? 0 : lo);
+  return len < 0 ? 0 : m;
+}
+
+// Largest raster width the row-diagonal prefill supports: its band pattern
+// (one 64-bit word per residue mod G) lives in LDS.
+constexpr int GMAX = 2048;
+
 // ---------------------------------------------------------------- tile lists
 // For query tile qt of batch b: the key tiles (BN keys) holding a kept pair,
 // in order, each with two 64-bit masks over (wave, row block, 16-key block)
@@ -145,7 +158,7 @@ __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------- attention
-template <int HD>
+template <int HD, int MODE>
 __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   constexpr int RB = RB_MAX;
   constexpr int NC = HD / 32;          // 32-wide contraction chunks of the head dim
@@ -159,6 +172,9 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   // ring of NS stages, each a K tile then a V tile, row-major, 16-byte
   // chunk p of row r holding the row's chunk p ^ (r % CPR) (bank spreading)
   __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * 2 * TILE];
+  // row-diagonal band pattern: bit c of bp[r] says whether a key c places
+  // before a query at residue r (mod G) lies within B of a multiple of G
+  __shared__ uint64_t bp[MODE == DA_MODE_ROWDIAG ? GMAX : 1];
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches
@@ -176,8 +192,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   const int n = a.n;
   const int P = clampi(a.prompt_len[b], 0, n);
   const int i_last = i0 + BM_ROWS - 1 < n - 1 ? i0 + BM_ROWS - 1 : n - 1;
-  const int mode = a.mode, W = a.W, Bw = a.B, G = a.G;
-  const bool all_residues = 2 * Bw + 1 >= G;
+  const int W = a.W, Bw = a.B, G = a.G;
   const int jt_max = (n - 1) / BN;
 
   const int64_t lid = (int64_t)b * a.n_qt + qt;
@@ -210,6 +225,22 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k)
     if (k < cnt) issue(list[2 * k].x, k);
+
+  if constexpr (MODE == DA_MODE_ROWDIAG) {
+    // band centres of residue r within reach of bits 0..63: r - kG for
+    // every k with r - kG in [-B, 63 + B]
+    for (int r = t; r < G; r += NTHREADS) {
+      uint64_t w = 0;
+      if (2 * Bw + 1 >= G) {
+        w = ~uint64_t(0);
+      } else {
+        int c0 = r;
+        while (c0 - G >= -Bw) c0 -= G;
+        for (; c0 <= 63 + Bw; c0 += G) w |= bit_range(c0 - Bw, c0 + Bw);
+      }
+      bp[r] = w;
+    }
+  }
 
   // ---- this wave's 16*RB query rows; lane lr of block rb holds row
   // wi0 + 16*rb + lr; its Q^T operand chunks stay in registers
@@ -263,8 +294,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   // tile t lives in stage t % NS; at the top of iteration idx tile idx+1
   // must have landed (tile idx+2 may still be in flight) and everyone must
   // be done with iteration idx-1, whose stage receives tile idx+3.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __builtin_amdgcn_s_barrier();
+  __syncthreads();                     // first tiles landed, band pattern written
   f32x4 sc_cur[RB][4];
   scores(ring, sc_cur);
   for (int idx = 0; idx < cnt; ++idx) {
@@ -275,9 +305,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
 
     const int4 e0 = list[2 * idx];
     const int4 e1 = list[2 * idx + 1];
-    const uint64_t need64 = (uint64_t)(uint32_t)e0.y | ((uint64_t)(uint32_t)e0.z << 32);
     const uint64_t full64 = (uint64_t)(uint32_t)e1.x | ((uint64_t)(uint32_t)e1.y << 32);
-    const unsigned needw = (unsigned)(need64 >> (wave * 8)) & 0xffu;
     const unsigned fullw = (unsigned)(full64 >> (wave * 8)) & 0xffu;
     const int j0 = clampi(e0.x, 0, jt_max) * BN;
     const uint16_t* vsm = ring + (idx % NS) * 2 * TILE + TILE;
@@ -289,33 +317,29 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
 
     scores(knext, sc_nxt);
 
-    // ---- masks of tile idx: empty blocks -> -inf, partial blocks -> rule
+    // ---- masks of tile idx (skipped when every block of this wave is
+    // wholly kept): a 64-bit keep word per row over the tile's keys --
+    // causal bits, prompt bits, and the window rule -- then each score the
+    // lane holds (key 16kq + 4lg + r) keeps its bits or becomes -inf
     if (fullw != 0xffu) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int i = my_i0 + 16 * rb;
+        const int x = my_i0 + 16 * rb - j0;           // row minus the tile's first key
+        uint64_t win;
+        if constexpr (MODE == DA_MODE_ROWDIAG) win = bp[mod_g(x, G, a.inv_g)] & bit_range(x - W, x);
+        else if constexpr (MODE == DA_MODE_BAND) win = bit_range(x - (Bw < W ? Bw : W), x);
+        else win = ~uint64_t(0);
+        const uint64_t keep = (win | bit_range(0, P - j0 - 1)) & bit_range(0, x);
+        const uint64_t sh = keep >> (4 * lg);
+        const uint32_t wd[2] = {(uint32_t)sh, (uint32_t)(sh >> 32)};
 #pragma unroll
-        for (int kq = 0; kq < 4; ++kq) {
-          const unsigned bit = 1u << (rb * 4 + kq);
-          const bool empty = !(needw & bit);
-          const bool partial = !empty && !(fullw & bit);
-          const int jb = j0 + 16 * kq + 4 * lg;       // element r is key jb + r
-          const int d0 = i - jb;
-          const int tm = (mode == DA_MODE_ROWDIAG && !all_residues) ? mod_g(d0 + Bw, G, a.inv_g) : 0;
+        for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int d = d0 - r;
-            bool kp = i < n && d >= 0;
-            if (mode != DA_MODE_DENSE && jb + r >= P) {
-              bool wk = d <= W;
-              if (mode == DA_MODE_BAND) wk = wk && d <= Bw;
-              else if (!all_residues) wk = wk && (tm - r < 0 ? tm - r + G : tm - r) <= 2 * Bw;
-              kp = kp && wk;
-            }
-            kp = !empty && (!partial || kp);
-            sc_cur[rb][kq][r] = kp ? sc_cur[rb][kq][r] : -INFINITY;
+            const int32_t m = (int32_t)(wd[kq >> 1] << (31 - (16 * (kq & 1) + r))) >> 31;
+            sc_cur[rb][kq][r] = __int_as_float((__float_as_int(sc_cur[rb][kq][r]) & m) |
+                                               (~m & (int32_t)0xff800000));
           }
-        }
       }
     }
 
@@ -468,6 +492,8 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
   if (!m->causal) return fail(DA_ENOTSUP, "prefill needs a causal mask");
   if (dtype != DA_BF16) return fail(DA_ENOTSUP, "prefill runs on bf16 inputs (dtype %d)", (int)dtype);
   if (head_dim != 64 && head_dim != 128) return fail(DA_ENOTSUP, "head_dim %d not in {64, 128}", head_dim);
+  if (m->mode == DA_MODE_ROWDIAG && m->G > GMAX)
+    return fail(DA_ENOTSUP, "row-diagonal prefill supports G <= %d (G=%d)", GMAX, m->G);
   if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads || n < 0)
     return fail(DA_EINVAL, "batch=%d heads=%d kv_heads=%d n=%d", batch, heads, kv_heads, n);
   if (!strides) return fail(DA_EINVAL, "strides is NULL");
@@ -497,9 +523,12 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
   a.qscale = scale * kLog2eP;
   const int64_t blocks = (int64_t)a.n_qt * batch * heads;
   if (blocks > 0x7fffffff) return fail(DA_ENOTSUP, "grid too large");
-  if (head_dim == 128)
-    hipLaunchKernelGGL(prefill_kernel<128>, dim3((unsigned)blocks), dim3(NTHREADS), 0, (hipStream_t)stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<64>, dim3((unsigned)blocks), dim3(NTHREADS), 0, (hipStream_t)stream, a);
+  void (*fn)(PrefillArgs);
+  switch (m->mode) {
+    case DA_MODE_DENSE: fn = head_dim == 128 ? prefill_kernel<128, DA_MODE_DENSE> : prefill_kernel<64, DA_MODE_DENSE>; break;
+    case DA_MODE_BAND: fn = head_dim == 128 ? prefill_kernel<128, DA_MODE_BAND> : prefill_kernel<64, DA_MODE_BAND>; break;
+    default: fn = head_dim == 128 ? prefill_kernel<128, DA_MODE_ROWDIAG> : prefill_kernel<64, DA_MODE_ROWDIAG>; break;
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(NTHREADS), 0, (hipStream_t)stream, a);
   return check_launch("prefill_kernel");
 }
