@@ -109,7 +109,37 @@ __device__ inline uint64_t bit_range(int lo, int hi) {
 
 // Largest raster width the row-diagonal prefill supports: its band pattern
 // (one 64-bit word per residue mod G) lives in LDS.
-constexpr int GMAX = 2048;
+constexpr int GMAX = 1024;
+
+// Longest tile list a query tile may have (LDS copy, 16 bytes an entry):
+// sequences of up to 64 * MAX_LIST tokens.
+constexpr int MAX_LIST = 1024;
+
+// 16-byte copy global -> LDS (global_load_lds_dwordx4; lane l's bytes land
+// at lds + 16 l).  Issued as inline assembly so that the compiler does not
+// treat it as a pending LDS write that every later LDS read must wait for:
+// the ring's own waits (vmcnt + barrier) order the stages.
+__device__ inline void dma16(const void* src, const void* lds) {
+  const uint32_t dst = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
+  __asm__ volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(dst) : "memory");
+}
+
+// Max across the lanes l, l ^ 16, l ^ 32 and l ^ 48 (VALU lane swaps).
+__device__ inline float max_over_row_groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum across the lanes l, l ^ 16, l ^ 32 and l ^ 48.
+__device__ inline float sum_over_row_groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // ---------------------------------------------------------------- tile lists
 // For query tile qt of batch b: the key tiles (BN keys) holding a kept pair,
@@ -175,6 +205,9 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   // row-diagonal band pattern: bit c of bp[r] says whether a key c places
   // before a query at residue r (mod G) lies within B of a multiple of G
   __shared__ uint64_t bp[MODE == DA_MODE_ROWDIAG ? GMAX : 1];
+  // this query tile's list: (key tile, full-block mask lo, hi, 0); read
+  // from LDS so that no list read waits behind the tile DMA in flight
+  __shared__ int4 tl[MAX_LIST];
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches
@@ -217,14 +250,21 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
       const int chunk = pos ^ (row % CPR);
       int j = jt * BN + row;
       j = j < n ? j : n - 1;                          // rows past the end: masked later
-      __builtin_amdgcn_global_load_lds(kb + (int64_t)j * a.sk[2] + chunk * 8, kd + blk * 512, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + (int64_t)j * a.sv[2] + chunk * 8, vd + blk * 512, 16, 0, 0);
+      dma16(kb + (int64_t)j * a.sk[2] + chunk * 8, kd + blk * 512);
+      dma16(vb + (int64_t)j * a.sv[2] + chunk * 8, vd + blk * 512);
     }
   };
 
+  for (int e = t; e < cnt; e += NTHREADS) {
+    const int4 e0 = list[2 * e];
+    const int4 e1 = list[2 * e + 1];
+    tl[e] = make_int4(clampi(e0.x, 0, jt_max), e1.x, e1.y, 0);
+  }
+  __syncthreads();
+
 #pragma unroll
   for (int k = 0; k < NS - 1; ++k)
-    if (k < cnt) issue(list[2 * k].x, k);
+    if (k < cnt) issue(tl[k].x, k);
 
   if constexpr (MODE == DA_MODE_ROWDIAG) {
     // band centres of residue r within reach of bits 0..63: r - kG for
@@ -301,13 +341,13 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
     if (idx + 2 < cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DPW));
     else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
-    if (idx + NS - 1 < cnt) issue(list[2 * (idx + NS - 1)].x, (idx + NS - 1) % NS);
+    __asm__ volatile("" ::: "memory");   // no ring read moves above the wait
+    if (idx + NS - 1 < cnt) issue(tl[idx + NS - 1].x, (idx + NS - 1) % NS);
 
-    const int4 e0 = list[2 * idx];
-    const int4 e1 = list[2 * idx + 1];
-    const uint64_t full64 = (uint64_t)(uint32_t)e1.x | ((uint64_t)(uint32_t)e1.y << 32);
+    const int4 e = tl[idx];
+    const uint64_t full64 = (uint64_t)(uint32_t)e.y | ((uint64_t)(uint32_t)e.z << 32);
     const unsigned fullw = (unsigned)(full64 >> (wave * 8)) & 0xffu;
-    const int j0 = clampi(e0.x, 0, jt_max) * BN;
+    const int j0 = e.x * BN;
     const uint16_t* vsm = ring + (idx % NS) * 2 * TILE + TILE;
 
     // scores of the next tile (its stage is resident; past the end this
@@ -352,8 +392,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
       for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc_cur[rb][kq][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_over_row_groups(mt);
       const float mts = mt * a.qscale;
       // the reference max only moves when a row's max grows by more than 2^8
       // (p <= 256 is exact enough in bf16 and fp32); whole wave or none
@@ -412,8 +451,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float L = ls[rb];
-    L += __shfl_xor(L, 16);
-    L += __shfl_xor(L, 32);
+    L = sum_over_row_groups(L);
     const int i = wi0 + 16 * rb + lr;
     if (i > i_last) continue;
     const float inv = 1.f / L;
@@ -492,6 +530,8 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
   if (!m->causal) return fail(DA_ENOTSUP, "prefill needs a causal mask");
   if (dtype != DA_BF16) return fail(DA_ENOTSUP, "prefill runs on bf16 inputs (dtype %d)", (int)dtype);
   if (head_dim != 64 && head_dim != 128) return fail(DA_ENOTSUP, "head_dim %d not in {64, 128}", head_dim);
+  if ((int64_t)n > (int64_t)BN * MAX_LIST)
+    return fail(DA_ENOTSUP, "prefill supports sequences of up to %d tokens (n=%d)", BN * MAX_LIST, n);
   if (m->mode == DA_MODE_ROWDIAG && m->G > GMAX)
     return fail(DA_ENOTSUP, "row-diagonal prefill supports G <= %d (G=%d)", GMAX, m->G);
   if (batch < 0 || heads < 1 || kv_heads < 1 || heads % kv_heads || n < 0)
