@@ -18,4 +18,5 @@ from .api import (  # noqa: F401
     mask,
     prefill_tiles_build,
     sparse_decode_attn,
+    sparse_decode_attn_masked,
 )

@@ -158,6 +158,55 @@ def sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     return out, lse
 
 
+def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
+                              v_cache: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor,
+                              prompt_len: torch.Tensor, *, cap: int, split: int,
+                              block_table: Optional[torch.Tensor] = None,
+                              scale: Optional[float] = None, out=None, lse=None,
+                              want_lse: bool = False, workspace=None, count=None, idx=None,
+                              want_lists: bool = False):
+    """Decode with the keep-set computed in the kernel from (pos, prompt_len,
+    mask) -- one launch for build + attention.  q [n_q, hq, hd]; caches as in
+    ``kv_cache``; seq/pos/prompt_len [n_q] int32.  With ``want_lists`` (or
+    given count/idx) the lists keepset_build would write are written too.
+    Returns (out, lse or None, count or None, idx or None)."""
+    _need_cuda("sparse_decode_attn_masked", q, k_cache, v_cache, seq, pos, prompt_len, block_table)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [n_q, hq, hd] tensor")
+    if q.dtype not in _DTYPE or q.dtype != k_cache.dtype:
+        raise ValueError("q and the caches must share dtype fp32 or bf16")
+    n_q, hq, hd = q.shape
+    hkv = k_cache.shape[1]
+    for t in (seq, pos, prompt_len):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != n_q:
+            raise ValueError("seq, pos and prompt_len must be contiguous int32 [n_q] tensors")
+    if scale is None:
+        scale = 1.0 / math.sqrt(hd)
+    if out is None:
+        out = torch.empty_like(q)
+    if want_lse and lse is None:
+        lse = torch.empty((n_q, hq), dtype=torch.float32, device=q.device)
+    if want_lists and count is None:
+        count = torch.empty(n_q, dtype=torch.int32, device=q.device)
+        idx = torch.empty((n_q, cap), dtype=torch.int32, device=q.device)
+    if (count is None) != (idx is None):
+        raise ValueError("count and idx go together")
+    if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous() or
+                            tuple(idx.shape) != (n_q, cap) or count.dtype != torch.int32):
+        raise ValueError("idx must be a contiguous int32 [n_q, cap] tensor, count int32 [n_q]")
+    if workspace is None:
+        workspace = decode_workspace(n_q, hq, hd, cap, split, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    kv = kv_cache(k_cache, v_cache, block_table)
+    check(load().da_sparse_decode_attn_masked(m, _ptr(q), _DTYPE[q.dtype], n_q, hq, hkv, hd,
+                                              float(scale), kv, _ptr(seq), _ptr(pos),
+                                              _ptr(prompt_len), cap, split, _ptr(count), _ptr(idx),
+                                              _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                                              _stream(q)),
+          "da_sparse_decode_attn_masked")
+    return out, lse, count, idx
+
+
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int,
                    nbytes: Optional[int] = None, offset: int = 0) -> None:
     """Streams `nbytes` bytes of `buf` starting at byte `offset` (measurement)."""

@@ -44,28 +44,39 @@ struct DecodeArgs {
   const int32_t* seq;
   const int32_t* count;
   const int32_t* idx;
+  // keep-set computed in the kernel (mask form): positions, prompt lengths,
+  // the mask, and optional list outputs (count may be null: no lists)
+  const int32_t* pos;
+  const int32_t* prompt;
+  int mode, W, B, G;
+  int32_t* count_out;
+  int32_t* idx_out;
   int n_q, hq, hkv, cap, split, max_split;
   float qscale;           // scale * log2(e)
   void* out;
   float* lse;
   float* ws_o;            // [n_q][hq][max_split][HD]
   float* ws_ml;           // [n_q][hq][max_split][2]
+  int32_t* ws_cnt;        // [n_q] keep-set sizes (mask form, several chunks)
+  const int32_t* mcount;  // the sizes the merge reads: count (lists) or ws_cnt
 };
 
-// Workspace layout: partial outputs, then partial (max, sum) pairs.
+// Workspace layout: partial outputs, then partial (max, sum) pairs, then
+// (mask form) each query's keep-set size for the merge.
 struct WsLayout {
-  int64_t o_off, ml_off, bytes;
+  int64_t o_off, ml_off, cnt_off, bytes;
 };
 
 static inline int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
 
 static WsLayout ws_layout(int64_t n_q, int64_t hq, int64_t hd, int64_t ns) {
-  WsLayout w{0, 0, 0};
+  WsLayout w{0, 0, 0, 0};
   if (ns <= 1) return w;
   const int64_t rows = n_q * hq * ns;
   w.o_off = 0;
   w.ml_off = align256(rows * hd * 4);
-  w.bytes = w.ml_off + align256(rows * 2 * 4);
+  w.cnt_off = w.ml_off + align256(rows * 2 * 4);
+  w.bytes = w.cnt_off + align256(n_q * 4);
   return w;
 }
 
@@ -138,7 +149,16 @@ __device__ inline float chunk_dot(const u32x4 q, const u32x4 k, const float* qf)
   }
 }
 
-template <bool BF16, int HD, int GRP, int NP>
+// Element offset of position j of request sq (contiguous or paged cache).
+__device__ inline int64_t row_offset(const DecodeArgs& a, const int32_t* bt, int sq, int j) {
+  j = clampi(j, 0, a.max_len - 1);
+  if (bt)
+    return (int64_t)clampi(bt[j >> a.ps_shift], 0, a.n_pages - 1) * a.page_stride +
+           (int64_t)(j & a.ps_mask) * a.slot_stride;
+  return (int64_t)sq * a.page_stride + (int64_t)j * a.slot_stride;
+}
+
+template <bool BF16, int HD, int GRP, int NP, bool MASKED>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   using TL = Tile<BF16, HD, NP>;
   constexpr int ES = TL::ES;
@@ -175,56 +195,126 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     qw[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.q) + qoff * ES);
   }
   constexpr int IPT = 4;                  // list entries per thread per round
-  int jj[IPT];
+  int cnt, nrows, sq;
+  const int32_t* bt;
+  int64_t off0;
+  if constexpr (!MASKED) {
+    int jj[IPT];
 #pragma unroll
-  for (int u = 0; u < IPT; ++u) {
-    const int r = u * 256 + t;
-    jj[u] = myidx[r < lim ? r : lim - 1];
-  }
-  int cnt = a.count[qi];
-  const int sq_raw = a.seq[qi];
-  // compiler-only barrier: keeps the loads above ahead of the count test
-  // (they would otherwise be sunk behind it); emits nothing
-  __asm__ volatile("" ::: "memory");
-  cnt = cnt < a.cap ? cnt : a.cap;
-  if (r0 >= cnt) return;
-  const int nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
-  const int sq = clampi(sq_raw, 0, a.n_seq - 1);
+    for (int u = 0; u < IPT; ++u) {
+      const int r = u * 256 + t;
+      jj[u] = myidx[r < lim ? r : lim - 1];
+    }
+    cnt = a.count[qi];
+    const int sq_raw = a.seq[qi];
+    // compiler-only barrier: keeps the loads above ahead of the count test
+    // (they would otherwise be sunk behind it); emits nothing
+    __asm__ volatile("" ::: "memory");
+    cnt = cnt < a.cap ? cnt : a.cap;
+    if (r0 >= cnt) return;
+    nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
+    sq = clampi(sq_raw, 0, a.n_seq - 1);
 
-  // ---- stage 1: element offset of every listed row into LDS
-  const int32_t* bt = a.block_table ? a.block_table + (int64_t)sq * a.bt_stride : nullptr;
-  const int64_t off0 = bt ? (int64_t)clampi(bt[0], 0, a.n_pages - 1) * a.page_stride
-                          : (int64_t)sq * a.page_stride;
-  for (int base = 0; base < nrows; base += IPT * 256) {
-    if (base > 0) {
+    // ---- stage 1: element offset of every listed row into LDS
+    bt = a.block_table ? a.block_table + (int64_t)sq * a.bt_stride : nullptr;
+    off0 = bt ? (int64_t)clampi(bt[0], 0, a.n_pages - 1) * a.page_stride
+              : (int64_t)sq * a.page_stride;
+    for (int base = 0; base < nrows; base += IPT * 256) {
+      if (base > 0) {
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) {
+          const int r = base + u * 256 + t;
+          jj[u] = myidx[r < lim ? r : lim - 1];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) jj[u] = clampi(jj[u], 0, a.max_len - 1);
+      int64_t o[IPT];
+      if (bt) {
+        int pg[IPT];
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) pg[u] = bt[jj[u] >> a.ps_shift];
+#pragma unroll
+        for (int u = 0; u < IPT; ++u)
+          o[u] = (int64_t)clampi(pg[u], 0, a.n_pages - 1) * a.page_stride +
+                 (int64_t)(jj[u] & a.ps_mask) * a.slot_stride;
+      } else {
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) o[u] = (int64_t)sq * a.page_stride + (int64_t)jj[u] * a.slot_stride;
+      }
 #pragma unroll
       for (int u = 0; u < IPT; ++u) {
         const int r = base + u * 256 + t;
-        jj[u] = myidx[r < lim ? r : lim - 1];
+        if (r < nrows) rowoff[r] = o[u];
       }
     }
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) jj[u] = clampi(jj[u], 0, a.max_len - 1);
-    int64_t o[IPT];
-    if (bt) {
-      int pg[IPT];
-#pragma unroll
-      for (int u = 0; u < IPT; ++u) pg[u] = bt[jj[u] >> a.ps_shift];
-#pragma unroll
-      for (int u = 0; u < IPT; ++u)
-        o[u] = (int64_t)clampi(pg[u], 0, a.n_pages - 1) * a.page_stride +
-               (int64_t)(jj[u] & a.ps_mask) * a.slot_stride;
-    } else {
-#pragma unroll
-      for (int u = 0; u < IPT; ++u) o[u] = (int64_t)sq * a.page_stride + (int64_t)jj[u] * a.slot_stride;
+    __syncthreads();
+  } else {
+    // ---- keep-set in the kernel: the same rule and order as the list
+    // builder.  Entries 0 .. Pc-1 are the prompt (or, DENSE, every key up to
+    // the query); the window [wlo, whi] follows, scanned 256 positions a
+    // round with a ballot per wave and a prefix over the four waves.  Every
+    // entry of this chunk gets its row offset in LDS; with list outputs,
+    // the kv-head-0 workgroups also write the entries of their chunk.
+    __shared__ int wcount[4];
+    const int i = a.pos[qi];
+    const int P = a.prompt[qi];
+    const int sq_raw = a.seq[qi];
+    __asm__ volatile("" ::: "memory");
+    sq = clampi(sq_raw, 0, a.n_seq - 1);
+    bt = a.block_table ? a.block_table + (int64_t)sq * a.bt_stride : nullptr;
+    off0 = bt ? (int64_t)clampi(bt[0], 0, a.n_pages - 1) * a.page_stride
+              : (int64_t)sq * a.page_stride;
+    const bool bad = i < 0 || P < 0;
+    const int L = i + 1;
+    int Pc = 0, wlo = 1, whi = 0;
+    if (!bad) {
+      if (a.mode == DA_MODE_DENSE) {
+        Pc = L;
+      } else {
+        Pc = P < L ? P : L;
+        wlo = i - a.W > Pc ? i - a.W : Pc;
+        whi = i;
+      }
     }
-#pragma unroll
-    for (int u = 0; u < IPT; ++u) {
-      const int r = base + u * 256 + t;
-      if (r < nrows) rowoff[r] = o[u];
+    const int lim_e = r0 + lim;                       // entries of this chunk: [r0, lim_e)
+    const bool lists = a.count_out != nullptr && g == 0;
+    int32_t* my_out = lists ? a.idx_out + (int64_t)qi * a.cap : nullptr;
+    for (int r = r0 + t; r < (Pc < lim_e ? Pc : lim_e); r += 256) {
+      rowoff[r - r0] = row_offset(a, bt, sq, r);
+      if (lists) my_out[r] = r;
     }
+    const int wave_id = t >> 6;
+    const int lane = t & 63;
+    const uint64_t below = (uint64_t(1) << lane) - 1;
+    int n = Pc;
+    for (int base = wlo; base <= whi; base += 256) {
+      const int j = base + t;
+      const bool kp = j <= whi && window_keep(a.mode, i - j, a.B, a.G);
+      const uint64_t bal = __ballot(kp);
+      if (lane == 0) wcount[wave_id] = __popcll(bal);
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        before += w < wave_id ? wcount[w] : 0;
+        total += wcount[w];
+      }
+      const int r = n + before + __popcll(bal & below);
+      if (kp && r >= r0 && r < lim_e) {
+        rowoff[r - r0] = row_offset(a, bt, sq, j);
+        if (lists) my_out[r] = j;
+      }
+      n += total;
+      __syncthreads();                                // wcount is reused
+    }
+    if (lists && s == 0 && t == 0) a.count_out[qi] = n;
+    if (a.ws_cnt && g == 0 && s == 0 && t == 0) a.ws_cnt[qi] = n;
+    cnt = n < a.cap ? n : a.cap;
+    __syncthreads();                                  // row offsets written
+    if (r0 >= cnt) return;
+    nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
   }
-  __syncthreads();
 
   // ---- query slices as fp32 (the fp32 path; bf16 uses the packed words)
   float qf[GRP][4];
@@ -373,7 +463,7 @@ __global__ void __launch_bounds__(64) merge_kernel(DecodeArgs a) {
   const int row = blockIdx.x;           // query * hq + head
   const int qi = row / a.hq;
   const int lane = threadIdx.x;
-  int cnt = a.count[qi];
+  int cnt = a.mcount[qi];
   cnt = cnt < a.cap ? cnt : a.cap;
   if (cnt <= a.split) return;           // written directly by decode_kernel
   const int ns = (cnt + a.split - 1) / a.split;
@@ -413,21 +503,28 @@ typedef void (*decode_fn)(DecodeArgs);
 typedef void (*merge_fn)(DecodeArgs);
 
 // Tile depth: NP passes per tile (two tiles in flight per workgroup).
-template <bool BF16, int HD, int GRP>
+template <bool BF16, int HD, int GRP, bool MASKED>
 static decode_fn pick_np(int np) {
-  if (np <= 2) return decode_kernel<BF16, HD, GRP, 2>;
-  if (np == 3) return decode_kernel<BF16, HD, GRP, 3>;
-  return decode_kernel<BF16, HD, GRP, 4>;
+  if (np <= 2) return decode_kernel<BF16, HD, GRP, 2, MASKED>;
+  if (np == 3) return decode_kernel<BF16, HD, GRP, 3, MASKED>;
+  return decode_kernel<BF16, HD, GRP, 4, MASKED>;
 }
 
-template <bool BF16, int HD>
+template <bool BF16, int HD, bool MASKED>
 static decode_fn pick_grp(int grp, int np) {
   switch (grp) {
-    case 1: return pick_np<BF16, HD, 1>(np);
-    case 2: return pick_np<BF16, HD, 2>(np);
-    case 4: return pick_np<BF16, HD, 4>(np);
-    default: return pick_np<BF16, HD, 8>(np);
+    case 1: return pick_np<BF16, HD, 1, MASKED>(np);
+    case 2: return pick_np<BF16, HD, 2, MASKED>(np);
+    case 4: return pick_np<BF16, HD, 4, MASKED>(np);
+    default: return pick_np<BF16, HD, 8, MASKED>(np);
   }
+}
+
+template <bool MASKED>
+static decode_fn pick_kernel(da_dtype dtype, int head_dim, int grp, int np) {
+  if (dtype == DA_BF16)
+    return head_dim == 64 ? pick_grp<true, 64, MASKED>(grp, np) : pick_grp<true, 128, MASKED>(grp, np);
+  return head_dim == 64 ? pick_grp<false, 64, MASKED>(grp, np) : pick_grp<false, 128, MASKED>(grp, np);
 }
 
 // Row slots past a list's end still issue their (redundant) loads, and on
@@ -453,24 +550,12 @@ constexpr int kMaxSplit = 4096;
 
 static int64_t n_splits(int32_t cap, int32_t split) { return (int64_t(cap) + split - 1) / split; }
 
-}  // namespace da
-
-using namespace da;
-
-extern "C" int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t head_dim,
-                                             int32_t cap, int32_t split) {
-  if (n_q < 0 || hq < 1 || head_dim < 1 || cap < 1 || split < 1)
-    return fail(DA_EINVAL, "workspace sizing: invalid sizes");
-  clear_error();
-  return ws_layout(n_q, hq, head_dim, n_splits(cap, split)).bytes;
-}
-
-extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q, int32_t hq,
-                                     int32_t hkv, int32_t head_dim, float scale,
-                                     const da_kv_cache* kv, const int32_t* seq,
-                                     const int32_t* count, const int32_t* idx, int32_t cap,
-                                     int32_t split, void* out, float* lse, void* workspace,
-                                     int64_t ws_bytes, void* stream) {
+// Checks the arguments shared by both decode entry points and fills `a`;
+// DA_OK or a negative status (nothing launched).
+static int prepare_decode(DecodeArgs& a, const void* q, da_dtype dtype, int32_t n_q, int32_t hq,
+                          int32_t hkv, int32_t head_dim, float scale, const da_kv_cache* kv,
+                          const int32_t* seq, int32_t cap, int32_t split, void* out, float* lse,
+                          void* workspace, int64_t ws_bytes) {
   if (n_q < 0) return fail(DA_EINVAL, "n_q=%d < 0", n_q);
   if (hq < 1 || hkv < 1 || hq % hkv) return fail(DA_EINVAL, "hq=%d hkv=%d: need hq %% hkv == 0", hq, hkv);
   if (!kv) return fail(DA_EINVAL, "kv descriptor is NULL");
@@ -494,8 +579,8 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
     return fail(DA_EINVAL, "max_len=%d exceeds bt_stride * page_size", kv->max_len);
   if (!kv->block_table && kv->n_pages < kv->n_seq)
     return fail(DA_EINVAL, "contiguous cache: n_pages must cover n_seq");
-  if (n_q > 0 && (!q || !out || !seq || !count || !idx || !kv->k || !kv->v))
-    return fail(DA_EINVAL, "q, out, seq, count, idx, kv->k and kv->v must be non-NULL");
+  if (n_q > 0 && (!q || !out || !seq || !kv->k || !kv->v))
+    return fail(DA_EINVAL, "q, out, seq, kv->k and kv->v must be non-NULL");
   const int esz = dtype == DA_BF16 ? 2 : 4;
   if (((kv->page_stride | kv->head_stride | kv->slot_stride) * esz) % 16 ||
       ((uintptr_t)kv->k | (uintptr_t)kv->v | (uintptr_t)q | (uintptr_t)out) % 16)
@@ -507,10 +592,8 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
   if (wl.bytes > 0 && (uintptr_t)workspace % 256) return fail(DA_EINVAL, "workspace not 256-byte aligned");
   const int64_t blocks = int64_t(n_q) * hkv * ns;
   if (blocks > 0x7fffffff) return fail(DA_ENOTSUP, "grid of %lld workgroups too large", (long long)blocks);
-  clear_error();
-  if (n_q == 0) return DA_OK;
 
-  DecodeArgs a;
+  a = DecodeArgs{};
   a.q = q;
   a.k = kv->k;
   a.v = kv->v;
@@ -525,8 +608,6 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
   a.n_pages = kv->n_pages;
   a.max_len = kv->max_len;
   a.seq = seq;
-  a.count = count;
-  a.idx = idx;
   a.n_q = n_q;
   a.hq = hq;
   a.hkv = hkv;
@@ -539,22 +620,88 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
   char* ws = reinterpret_cast<char*>(workspace);
   a.ws_o = wl.bytes ? reinterpret_cast<float*>(ws + wl.o_off) : nullptr;
   a.ws_ml = wl.bytes ? reinterpret_cast<float*>(ws + wl.ml_off) : nullptr;
+  a.ws_cnt = wl.bytes ? reinterpret_cast<int32_t*>(ws + wl.cnt_off) : nullptr;
+  return DA_OK;
+}
 
-  const int chunk = split < cap ? split : cap;
+// Launches the decode kernel (and, when a list spans several chunks, the
+// merge) for prepared arguments.
+template <bool MASKED>
+static int launch_decode(const DecodeArgs& a, da_dtype dtype, int head_dim, void* stream) {
+  const int esz = dtype == DA_BF16 ? 2 : 4;
+  const int chunk = a.split < a.cap ? a.split : a.cap;
   const int np = tile_depth(chunk, 256 / (head_dim * esz / 16));
-  decode_fn dk;
-  merge_fn mk;
-  if (dtype == DA_BF16) {
-    dk = head_dim == 64 ? pick_grp<true, 64>(grp, np) : pick_grp<true, 128>(grp, np);
-    mk = head_dim == 64 ? merge_kernel<true, 64> : merge_kernel<true, 128>;
-  } else {
-    dk = head_dim == 64 ? pick_grp<false, 64>(grp, np) : pick_grp<false, 128>(grp, np);
-    mk = head_dim == 64 ? merge_kernel<false, 64> : merge_kernel<false, 128>;
-  }
+  const decode_fn dk = pick_kernel<MASKED>(dtype, head_dim, a.hq / a.hkv, np);
+  const merge_fn mk = dtype == DA_BF16 ? (head_dim == 64 ? merge_kernel<true, 64> : merge_kernel<true, 128>)
+                                       : (head_dim == 64 ? merge_kernel<false, 64> : merge_kernel<false, 128>);
+  const int64_t blocks = int64_t(a.n_q) * a.hkv * a.max_split;
   const size_t lds = (size_t)chunk * sizeof(int64_t);
   hipLaunchKernelGGL(dk, dim3((unsigned)blocks), dim3(256), lds, (hipStream_t)stream, a);
   int rc = check_launch("decode_kernel");
-  if (rc || ns <= 1) return rc;
-  hipLaunchKernelGGL(mk, dim3((unsigned)(int64_t(n_q) * hq)), dim3(64), 0, (hipStream_t)stream, a);
+  if (rc || a.max_split <= 1) return rc;
+  hipLaunchKernelGGL(mk, dim3((unsigned)(int64_t(a.n_q) * a.hq)), dim3(64), 0, (hipStream_t)stream, a);
   return check_launch("merge_kernel");
+}
+
+}  // namespace da
+
+using namespace da;
+
+extern "C" int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t head_dim,
+                                             int32_t cap, int32_t split) {
+  if (n_q < 0 || hq < 1 || head_dim < 1 || cap < 1 || split < 1)
+    return fail(DA_EINVAL, "workspace sizing: invalid sizes");
+  clear_error();
+  return ws_layout(n_q, hq, head_dim, n_splits(cap, split)).bytes;
+}
+
+extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q, int32_t hq,
+                                     int32_t hkv, int32_t head_dim, float scale,
+                                     const da_kv_cache* kv, const int32_t* seq,
+                                     const int32_t* count, const int32_t* idx, int32_t cap,
+                                     int32_t split, void* out, float* lse, void* workspace,
+                                     int64_t ws_bytes, void* stream) {
+  DecodeArgs a;
+  int rc = prepare_decode(a, q, dtype, n_q, hq, hkv, head_dim, scale, kv, seq, cap, split, out, lse,
+                          workspace, ws_bytes);
+  if (rc) return rc;
+  if (n_q > 0 && (!count || !idx)) return fail(DA_EINVAL, "count and idx must be non-NULL");
+  clear_error();
+  if (n_q == 0) return DA_OK;
+  a.count = count;
+  a.idx = idx;
+  a.mcount = count;
+  a.ws_cnt = nullptr;                   // the merge reads the lists' counts
+  return launch_decode<false>(a, dtype, head_dim, stream);
+}
+
+extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_dtype dtype,
+                                            int32_t n_q, int32_t hq, int32_t hkv, int32_t head_dim,
+                                            float scale, const da_kv_cache* kv, const int32_t* seq,
+                                            const int32_t* pos, const int32_t* prompt_len,
+                                            int32_t cap, int32_t split, int32_t* count, int32_t* idx,
+                                            void* out, float* lse, void* workspace, int64_t ws_bytes,
+                                            void* stream) {
+  int rc = check_mask(m);
+  if (rc) return rc;
+  if (!m->causal) return fail(DA_ENOTSUP, "decode needs a causal mask");
+  DecodeArgs a;
+  rc = prepare_decode(a, q, dtype, n_q, hq, hkv, head_dim, scale, kv, seq, cap, split, out, lse,
+                      workspace, ws_bytes);
+  if (rc) return rc;
+  if (n_q > 0 && (!pos || !prompt_len)) return fail(DA_EINVAL, "pos and prompt_len must be non-NULL");
+  if ((count == nullptr) != (idx == nullptr))
+    return fail(DA_EINVAL, "count and idx must both be given or both be NULL");
+  clear_error();
+  if (n_q == 0) return DA_OK;
+  a.pos = pos;
+  a.prompt = prompt_len;
+  a.mode = m->mode;
+  a.W = m->W;
+  a.B = m->B;
+  a.G = m->G;
+  a.count_out = count;
+  a.idx_out = idx;
+  a.mcount = a.ws_cnt;                  // written by the decode kernel when there is a merge
+  return launch_decode<true>(a, dtype, head_dim, stream);
 }

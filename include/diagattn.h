@@ -185,6 +185,38 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
                           int32_t split, void* out, float* lse,
                           void* workspace, int64_t ws_bytes, void* stream);
 
+/* sparse_decode_attn_masked -- the same decode step with the keep-set taken
+ * from the mask instead of lists: keep-set build and attention in one launch.
+ *
+ * For query q the kept keys are the keep-set of position pos[q] with
+ * prompt_len[q] prompt tokens under `m` (causal form), in the order and with
+ * the truncation of da_keepset_build: entries r < min(count, cap).  The
+ * output is then exactly that of da_sparse_decode_attn on the lists
+ * da_keepset_build would write (the same rows in the same order through the
+ * same kernel).  Rule and example as for da_keepset_build (the summary's M,
+ * prompt columns, row-offset diagonals; worked example).
+ *
+ *   m      [host] mask; m->causal must be 1
+ *   pos, prompt_len [n_q] int32 position and prompt length of each query
+ *   count, idx  optional outputs (both or neither): the lists exactly as
+ *          da_keepset_build writes them (count[q] the true size; idx[q*cap+r]
+ *          for r < min(count[q], cap)), for callers that reuse them
+ *   other arguments as for da_sparse_decode_attn (cap bounds the entries a
+ *          query attends to and sizes the chunk grid with `split`).
+ * Device data: pos[q] < 0 or prompt_len[q] < 0 gives count 0 and no output
+ * written for that query; positions and requests are clamped into the
+ * descriptor's extents.
+ * Errors: as da_sparse_decode_attn, plus DA_EINVAL for an invalid mask, null
+ * pos/prompt_len, or only one of count/idx given, DA_ENOTSUP for causal = 0. */
+int da_sparse_decode_attn_masked(const da_mask* m /* [host] */, const void* q,
+                                 da_dtype dtype, int32_t n_q, int32_t hq, int32_t hkv,
+                                 int32_t head_dim, float scale,
+                                 const da_kv_cache* kv /* [host] */, const int32_t* seq,
+                                 const int32_t* pos, const int32_t* prompt_len,
+                                 int32_t cap, int32_t split, int32_t* count, int32_t* idx,
+                                 void* out, float* lse, void* workspace, int64_t ws_bytes,
+                                 void* stream);
+
 /* [host] Bytes of the prefill tile lists for `batch` sequences of n tokens. */
 int64_t da_prefill_tiles_bytes(int32_t batch, int32_t n);
 
