@@ -1,27 +1,26 @@
 // band_prefill_attn: causal, keep-set-masked attention over whole sequences,
 // bf16 in, fp32 accumulation, on the matrix cores (v_mfma_f32_16x16x32_bf16).
 //
-// Workgroup = 4 waves = BM = 64*RB query rows of one (batch, head); each wave
-// owns 16*RB rows.  Key tiles of 64 rows are staged in LDS -- K row-major,
-// V transposed -- while the next kept tile is already being fetched into
-// registers.  Scores are computed transposed, S^T = K Q^T (A = K from LDS,
-// B = Q^T from registers), so that the MFMA result gives every lane one query
-// row and four keys of each 16-key block.  That lane-per-row layout is kept
-// for the whole softmax: the running max/sum are per lane (combined over the
-// four lanes of a row by two xor shuffles), the probabilities P^T are
-// already in the B-operand layout of the second product, and the output is
-// accumulated transposed, O^T += V^T P^T (A = V^T from LDS), so the online
-// rescale is one multiply per lane register.  The contraction index of both
-// products is assigned to lanes the same way on both operands, which is all
-// the MFMA needs.
+// Workgroup = 8 waves = 256 query rows of one (batch, head); each wave owns
+// two blocks of 16 rows.  The 64-key tiles that hold a kept pair (listed
+// once per query tile by prefill_tiles_kernel) stream K and V into a ring of
+// LDS stages by direct global->LDS copies, three tiles ahead.  Scores are
+// computed transposed, S^T = K Q^T (A = K from LDS, B = Q^T from
+// registers), so that the MFMA result gives every lane one query row and
+// four keys of each 16-key block.  That lane-per-row layout is kept for the
+// whole softmax: the running max/sum are per lane (combined over the four
+// lanes of a row by lane swaps), the probabilities P^T are already in the B
+// operand layout of the second product, and the output is accumulated
+// transposed, O^T += V^T P^T (A = V^T by transposing LDS reads of row-major
+// V), so the online rescale is one multiply per lane register.
 //
-// Sparsity: a 64-key tile is visited only if some (row, key) pair in it is
-// kept; inside a visited tile each wave skips 16-key blocks with no kept
-// pair for its rows, and element masks are applied only to blocks that are
-// not entirely kept.  Workgroups are numbered so that all query tiles of one
-// (batch, head) share an XCD (hardware dispatches workgroups to the 8 XCDs
-// round-robin), which keeps the prompt keys/values every tile re-reads in
-// that XCD's L2.
+// Sparsity: only listed key tiles are visited.  Inside one, a wave whose
+// blocks are all wholly kept applies no mask; otherwise each row gets a
+// 64-bit keep word over the tile's keys (causal, prompt and window bits)
+// and every score keeps its bit or becomes -inf.  Workgroups are numbered so
+// that all query tiles of one (batch, head) share an XCD (hardware deals
+// workgroups to the 8 XCDs round-robin), which keeps the prompt keys/values
+// every tile re-reads in that XCD's L2.
 #include "common.h"
 
 namespace da {
