@@ -237,20 +237,33 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
 
   // DMA of key tile jt into ring stage st: this wave's DPW transfers of K
   // and of V; lane l of transfer u fills LDS chunk l of its 1 KiB block
+  // this lane's rows of a tile and their element offsets (fixed per lane);
+  // a tile adds its first key's offset, rows past the end read the last row
+  int dma_row[DPW];
+  int64_t dma_k[DPW], dma_v[DPW], last_k[DPW], last_v[DPW];
+#pragma unroll
+  for (int u = 0; u < DPW; ++u) {
+    const int blk = wave * DPW + u;                   // 1 KiB block of the tile
+    const int row = blk * RPI + lane / CPR;
+    const int chunk = (lane % CPR) ^ (row % CPR);
+    dma_row[u] = row;
+    dma_k[u] = (int64_t)row * a.sk[2] + chunk * 8;
+    dma_v[u] = (int64_t)row * a.sv[2] + chunk * 8;
+    last_k[u] = (int64_t)(n - 1) * a.sk[2] + chunk * 8;
+    last_v[u] = (int64_t)(n - 1) * a.sv[2] + chunk * 8;
+  }
   auto issue = [&](int jt, int st) {
     jt = clampi(jt, 0, jt_max);
     uint16_t* kd = ring + st * 2 * TILE;
     uint16_t* vd = kd + TILE;
+    const int j0 = jt * BN;
+    const int64_t bk = (int64_t)j0 * a.sk[2], bv = (int64_t)j0 * a.sv[2];
 #pragma unroll
     for (int u = 0; u < DPW; ++u) {
-      const int blk = wave * DPW + u;                 // 1 KiB block of the tile
-      const int row = blk * RPI + lane / CPR;
-      const int pos = lane % CPR;
-      const int chunk = pos ^ (row % CPR);
-      int j = jt * BN + row;
-      j = j < n ? j : n - 1;                          // rows past the end: masked later
-      dma16(kb + (int64_t)j * a.sk[2] + chunk * 8, kd + blk * 512);
-      dma16(vb + (int64_t)j * a.sv[2] + chunk * 8, vd + blk * 512);
+      const int blk = wave * DPW + u;
+      const bool in = j0 + dma_row[u] < n;
+      dma16(kb + (in ? bk + dma_k[u] : last_k[u]), kd + blk * 512);
+      dma16(vb + (in ? bv + dma_v[u] : last_v[u]), vd + blk * 512);
     }
   };
 
@@ -382,8 +395,13 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // ---- online softmax (lazy reference max) and P^T operands
-    bf16x8 pb[RB][2];
+    // ---- online softmax (lazy reference max) and P^T operands.  The tile
+    // maxima of both row blocks come first and share one (rare) rescale
+    // branch, so that every exponential lands in the same block as the P.V
+    // products below.  The reference max only moves when a row's max grows
+    // by more than 2^8 (p <= 256 is exact enough in bf16 and fp32).
+    float mts[RB];
+    bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float mt = -INFINITY;
@@ -391,12 +409,13 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
       for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc_cur[rb][kq][r]);
-      mt = max_over_row_groups(mt);
-      const float mts = mt * a.qscale;
-      // the reference max only moves when a row's max grows by more than 2^8
-      // (p <= 256 is exact enough in bf16 and fp32); whole wave or none
-      if (__any(mts > mq[rb] + 8.f)) {
-        const float mn = fmaxf(mq[rb], mts);
+      mts[rb] = max_over_row_groups(mt) * a.qscale;
+      grow = grow || mts[rb] > mq[rb] + 8.f;
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float mn = fmaxf(mq[rb], mts[rb]);
         const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mq[rb] - mn);
         ls[rb] *= alpha;
 #pragma unroll
@@ -405,6 +424,10 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
           for (int r = 0; r < 4; ++r) o[rb][nb][r] *= alpha;
         mq[rb] = mn;
       }
+    }
+    bf16x8 pb[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
       const float mref = mq[rb] == -INFINITY ? 0.f : mq[rb];
       // slot e of 32-key chunk cc is key 32cc + (e/4)*16 + 4lg + e%4
 #pragma unroll
