@@ -124,6 +124,18 @@ __device__ inline void dma16(const void* src, const void* lds) {
   __asm__ volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(dst) : "memory");
 }
 
+// LDS position of 16-byte chunk p of key row r is p ^ swz(r).  With 16
+// chunks a row (head_dim 128) swz spreads both read patterns over all 64
+// banks: the K reads (16 consecutive rows, one chunk: swz is a permutation
+// of 0..15) and the transposing V reads (8 consecutive rows, two adjacent
+// chunks 2m, 2m+1: swz takes distinct values >> 1 on each aligned 8 rows
+// and keeps bit 0 fixed there).  With 8 chunks (head_dim 64) it is r % 8.
+template <int CPR>
+__device__ inline int swz(int r) {
+  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return r % CPR;
+}
+
 // Max across the lanes l, l ^ 16, l ^ 32 and l ^ 48 (VALU lane swaps).
 __device__ inline float max_over_row_groups(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -199,7 +211,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   constexpr int NS = 4;                // LDS ring stages (see the loop below)
 
   // ring of NS stages, each a K tile then a V tile, row-major, 16-byte
-  // chunk p of row r holding the row's chunk p ^ (r % CPR) (bank spreading)
+  // chunk p of row r holding the row's chunk p ^ swz(r) (bank spreading)
   __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * 2 * TILE];
   // row-diagonal band pattern: bit c of bp[r] says whether a key c places
   // before a query at residue r (mod G) lies within B of a multiple of G
@@ -245,7 +257,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   for (int u = 0; u < DPW; ++u) {
     const int blk = wave * DPW + u;                   // 1 KiB block of the tile
     const int row = blk * RPI + lane / CPR;
-    const int chunk = (lane % CPR) ^ (row % CPR);
+    const int chunk = (lane % CPR) ^ swz<CPR>(row);
     dma_row[u] = row;
     dma_k[u] = (int64_t)row * a.sk[2] + chunk * 8;
     dma_v[u] = (int64_t)row * a.sv[2] + chunk * 8;
@@ -331,7 +343,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
       const int row = 16 * kq + lr;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const int pos = (4 * c + lg) ^ (row % CPR);
+        const int pos = (4 * c + lg) ^ swz<CPR>(row);
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ksm + row * HD + pos * 8);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -451,8 +463,8 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
         typedef short v4i16 __attribute__((ext_vector_type(4)));
         const int chunk = 2 * nb + (vt_sub >> 1);
         const int r_lo = 32 * cc + vt_row, r_hi = r_lo + 16;
-        const uint16_t* plo = vsm + r_lo * HD + ((chunk ^ (r_lo % CPR)) * 8) + (vt_sub & 1) * 4;
-        const uint16_t* phi = vsm + r_hi * HD + ((chunk ^ (r_hi % CPR)) * 8) + (vt_sub & 1) * 4;
+        const uint16_t* plo = vsm + r_lo * HD + ((chunk ^ swz<CPR>(r_lo)) * 8) + (vt_sub & 1) * 4;
+        const uint16_t* phi = vsm + r_hi * HD + ((chunk ^ swz<CPR>(r_hi)) * 8) + (vt_sub & 1) * 4;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
         const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
         typedef short v8i16 __attribute__((ext_vector_type(8)));
