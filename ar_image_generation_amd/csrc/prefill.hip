@@ -125,11 +125,13 @@ __device__ inline void dma16(const void* src, const void* lds) {
 }
 
 // LDS position of 16-byte chunk p of key row r is p ^ swz(r).  With 16
-// chunks a row (head_dim 128) swz spreads both read patterns over all 64
-// banks: the K reads (16 consecutive rows, one chunk: swz is a permutation
-// of 0..15) and the transposing V reads (8 consecutive rows, two adjacent
-// chunks 2m, 2m+1: swz takes distinct values >> 1 on each aligned 8 rows
-// and keeps bit 0 fixed there).  With 8 chunks (head_dim 64) it is r % 8.
+// chunks a row (head_dim 128), under a model of 64 four-byte banks, swz
+// spreads both read patterns over all banks: the K reads (16 consecutive
+// rows, one chunk: swz is a permutation of 0..15) and the transposing V
+// reads (8 consecutive rows, two adjacent chunks 2m, 2m+1: swz takes
+// distinct values >> 1 on each aligned 8 rows and keeps bit 0 fixed).  The
+// bank-conflict counter did not drop with it, so that model is not the
+// whole story on this part.  With 8 chunks (head_dim 64) it is r % 8.
 template <int CPR>
 __device__ inline int swz(int r) {
   if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);

@@ -717,7 +717,8 @@ def main():
                        "frac_of_peak": round(kept / probe_us / 1e3 / HBM_PEAK_GBPS, 4),
                        "step_frac_of_attainable": round(probe_us / us_step, 4)},
         "cpu_baseline": cpu,
-        "device": torch.cuda.get_device_properties(0).name,
+        "device": f"{torch.cuda.get_device_properties(0).name} "
+                  f"{getattr(torch.cuda.get_device_properties(0), 'gcnArchName', '')}".strip(),
         "kept_MB_per_step": round(kept / 1e6, 3),
         "list_path": {"us_per_step": round(us_step_l, 2),
                       "tokens_per_s": round(b.n_q / (us_step_l * 1e-6), 1),
