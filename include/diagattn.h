@@ -142,9 +142,10 @@ typedef struct {
   int32_t max_len;
 } da_kv_cache;
 
-/* [host] Workspace bytes da_sparse_decode_attn needs for these sizes (0 when
- * every keep-set fits one chunk, i.e. cap <= split): the per-chunk partial
- * results (max, sum, unnormalised output) that the merge kernel combines. */
+/* [host] Workspace bytes da_sparse_decode_attn and da_sparse_decode_attn_masked
+ * need for these sizes (0 when every keep-set fits one chunk, i.e. cap <=
+ * split): the per-chunk partial results (max, sum, unnormalised output) that
+ * the merge kernel combines, and (mask form) each query's keep-set size. */
 int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t head_dim,
                                   int32_t cap, int32_t split);
 
@@ -253,8 +254,8 @@ int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t
  * apply the sparsity to decode, and this call serves the same mask where a
  * whole sequence is attended at once.  Only the key tiles listed in `tiles`
  * (da_prefill_tiles_build with the same mask, n and prompt_len) are
- * computed, by the waves whose rows they hold kept pairs for; element masks
- * are applied inside blocks that are not entirely kept.
+ * computed; element masks (a 64-bit keep word per row and key tile) are
+ * applied where a wave's blocks are not all entirely kept.
  *
  *   q, out [batch][heads][n][head_dim], k, v [batch][kv_heads][n][head_dim],
  *          bf16, head_dim elements contiguous and 16-byte aligned;
@@ -266,8 +267,11 @@ int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t
  * bf16 for the second product; outputs round to nearest even.  Tile entries
  * and counts are clamped into range, so an inconsistent list gives wrong
  * numbers, never an out-of-bounds access.
+ * Limits (LDS copies of the tile list and of the row-diagonal band pattern):
+ * n <= 65536 tokens; in ROWDIAG mode G <= 1024.
  * Errors: DA_EINVAL (mask, null pointers, sizes, strides, alignment),
- * DA_ENOTSUP (causal = 0, dtype other than bf16, head_dim not 64/128). */
+ * DA_ENOTSUP (causal = 0, dtype other than bf16, head_dim not 64/128,
+ * n > 65536, ROWDIAG with G > 1024). */
 int da_band_prefill_attn(const da_mask* m /* [host] */, da_dtype dtype, int32_t batch,
                          int32_t heads, int32_t kv_heads, int32_t n, int32_t head_dim,
                          const void* q, const void* k, const void* v, void* out,

@@ -117,6 +117,24 @@ def test_argument_errors_are_reported_before_launch():
     assert dec_m(n_q=0, pos=None) == 0     # nothing to do, nothing read
 
 
+def test_prefill_limits_are_reported_before_launch():
+    lib = da.load()
+    dummy = ctypes.c_void_p(256)   # never dereferenced: checks fail first
+    strides = (ctypes.c_int64 * 12)(*([128 * 1024, 128 * 1024, 128] * 4))
+
+    def pf(mk, n=1024, hd=128, dtype=1):
+        return lib.da_band_prefill_attn(mk, dtype, 1, 2, 2, n, hd, dummy, dummy, dummy, dummy,
+                                        strides, dummy, dummy, 0.1, None, None)
+    rd = da.mask(O.ROWDIAG, 64, 1, 32)
+    assert pf(rd, n=70000) == -2 and "65536" in _native.last_error()
+    assert pf(da.mask(O.ROWDIAG, 64, 1, 2048)) == -2 and "G <=" in _native.last_error()
+    assert pf(da.mask(O.BAND, 64, 1, 2048), n=0) == 0          # G only matters for ROWDIAG
+    assert pf(rd, hd=96) == -2
+    assert pf(rd, dtype=0) == -2
+    assert pf(da.mask(O.ROWDIAG, 64, 1, 32, causal=False)) == -2
+    assert pf(rd, n=0) == 0
+
+
 def test_decode_workspace_size():
     assert da.decode_workspace_bytes(4, 8, 128, 64, 64) == 0
     b = da.decode_workspace_bytes(4, 8, 128, 200, 64)
