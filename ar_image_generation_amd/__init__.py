@@ -17,6 +17,8 @@ from .api import (  # noqa: F401
     kv_cache,
     mask,
     prefill_tiles_build,
+    ring_block_table,
+    ring_pages,
     sparse_decode_attn,
     sparse_decode_attn_masked,
 )

@@ -8,6 +8,7 @@ runs in the library's HIP kernels.
 """
 from __future__ import annotations
 
+import ctypes
 import math
 from typing import Optional
 
@@ -205,6 +206,29 @@ def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
                                               _stream(q)),
           "da_sparse_decode_attn_masked")
     return out, lse, count, idx
+
+
+def ring_pages(m: DaMask, prompt_len: int, max_len: int, page_size: int) -> int:
+    """KV pages one request needs when rows older than the live window are
+    recycled (prompt pages plus a ring of window pages)."""
+    r = load().da_ring_pages(m, int(prompt_len), int(max_len), int(page_size))
+    check(r if r < 0 else 0, "da_ring_pages")
+    return int(r)
+
+
+def ring_block_table(m: DaMask, prompt_len, max_len: int, page_size: int, first_page: int = 0):
+    """Static block table whose window pages form a ring per request.
+    prompt_len: host ints [n_seq].  Returns (int32 CPU tensor [n_seq,
+    ceil(max_len / page_size)], total pages)."""
+    p = torch.as_tensor(prompt_len, dtype=torch.int32).contiguous()
+    n_seq = p.numel()
+    stride = -(-int(max_len) // int(page_size))
+    bt = torch.empty((n_seq, stride), dtype=torch.int32)
+    total = ctypes.c_int64(0)
+    check(load().da_ring_block_table(m, n_seq, p.data_ptr(), int(max_len), int(page_size),
+                                     int(first_page), stride, bt.data_ptr(), ctypes.byref(total)),
+          "da_ring_block_table")
+    return bt, int(total.value)
 
 
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int,

@@ -44,10 +44,34 @@ def kv_bytes_per_key(cfg):
     return cfg.hkv * 2 * cfg.hd * esz        # K and V rows of every kv head
 
 
+def ring_inputs(inp, m, page_size=16):
+    """Replaces the cache of `inp` by a ring-paged one (rows older than the
+    live window recycled, da.ring_block_table), filled the way generation
+    would fill it: each request's logical pages in order, later pages
+    overwriting their slot.  One query per request."""
+    import torch
+    import ar_image_generation_amd as da
+    k_log, v_log = inp.k_logical, inp.v_logical
+    n_seq, hkv, L, hd = k_log.shape
+    prompt = [int(inp.prompt_len[inp.seq == s][0]) for s in range(n_seq)]
+    bt, total = da.ring_block_table(m, prompt, L, page_size)
+    kc = torch.zeros((total, hkv, page_size, hd), dtype=k_log.dtype)
+    vc = torch.zeros_like(kc)
+    for s in range(n_seq):
+        top = int(inp.pos[inp.seq == s].max())
+        for lp in range(top // page_size + 1):
+            pg = int(bt[s, lp])
+            lo, hi = lp * page_size, min(L, (lp + 1) * page_size)
+            kc[pg, :, : hi - lo] = k_log[s, :, lo:hi]
+            vc[pg, :, : hi - lo] = v_log[s, :, lo:hi]
+    inp.k_cache, inp.v_cache, inp.block_table = kc, vc, bt
+    return total, n_seq * -(-L // page_size)
+
+
 class DecodeBench:
     """Device-resident inputs of one decode workload plus rotation copies."""
 
-    def __init__(self, cfg, n_copies=None, split=None):
+    def __init__(self, cfg, n_copies=None, split=None, ring=False):
         import torch
         import ar_image_generation_amd as da
         import workloads as wl
@@ -63,7 +87,10 @@ class DecodeBench:
         self.q = inp.q.to(dev)
         self.pos = inp.pos.to(dev)
         self.prompt = inp.prompt_len.to(dev)
-        self.paged = cfg.page_size > 0
+        self.paged = cfg.page_size > 0 or ring
+        self.ring_pages = None
+        if ring:
+            self.ring_pages = ring_inputs(inp, da.mask(cfg.modes[0], cfg.W, cfg.B, cfg.G))
         k = (inp.k_cache if self.paged else inp.k_logical)
         v = (inp.v_cache if self.paged else inp.v_logical)
         copy_bytes = 2 * k.numel() * k.element_size()
@@ -650,6 +677,31 @@ def main():
     value = b.n_q / (us_step * 1e-6)
     traffic = traffic_from_profile(cfg.name)
 
+    # keep-set-aware KV residency: the same step through a ring block table
+    residency = {}
+    if not args.no_extra:
+        b.decode_masked(mode, 0)
+        torch.cuda.synchronize()
+        ref_out = b.out.clone()
+        for name in ("llamagen_b16", "paged_b128"):
+            c = wl.CONFIGS[name]
+            rb = DecodeBench(c, ring=True)
+            md = c.modes[0]
+            st = rb.time_graph(md, K, W, path="fused")
+            total, full = rb.ring_pages
+            rec = {"mode": wl.MODE_NAMES[md], "pages_full": full, "pages_ring": total,
+                   "kv_bytes_ratio": round(total / full, 4), "us_per_step": round(st, 2),
+                   "kept_GBps": round(rb.kept_bytes(md) / (st * 1e-6) / 1e9, 1)}
+            if name == cfg.name:
+                rb.decode_masked(md, 0)
+                torch.cuda.synchronize()
+                rec["output_equals_full_cache"] = bool(torch.equal(rb.out, ref_out))
+            residency[name] = rec
+            log(f"[bench] {name} ring cache: {total} of {full} pages ({total / full:.3f}), "
+                f"fused step {st:.2f} us")
+            del rb
+            torch.cuda.empty_cache()
+
     extra = {}
     if not args.no_extra:
         for name in ("gqa_b64", "paged_b128"):
@@ -732,6 +784,7 @@ def main():
                   "speedup_step": round(us_step_d / us_step, 3),
                   "speedup_decode": round(us_dec_d / us_dec, 3)},
         "extra": extra,
+        "kv_residency": residency,
         "prefill": prefill,
     }
     print(json.dumps(line), flush=True)

@@ -218,6 +218,41 @@ int da_sparse_decode_attn_masked(const da_mask* m /* [host] */, const void* q,
                                  void* out, float* lse, void* workspace, int64_t ws_bytes,
                                  void* stream);
 
+/* KV residency.  Under the keep-set rule a decode query at position i reads
+ * prompt keys and keys j >= i - W (the summary's M, core formulas; BAND also
+ * needs |i - j| <= B, so only j >= i - min(B, W)), and later queries only
+ * move that window forward.  Rows older than the window are therefore dead
+ * once a request has passed them, and a request needs its prompt pages plus
+ * a ring of R = ceil((Wlive + 1) / page_size) + 1 window pages (Wlive = W,
+ * or min(B, W) for BAND) instead of one page per position.  DENSE keeps
+ * every page.
+ *
+ * [host] da_ring_pages: pages one request needs, for prompt_len prompt
+ * tokens and up to max_len positions: ceil(prompt_len / page_size) + R,
+ * capped at ceil(max_len / page_size).  Negative da_status on bad arguments
+ * (DA_ENOTSUP for causal = 0). */
+int64_t da_ring_pages(const da_mask* m /* [host] */, int32_t prompt_len, int32_t max_len,
+                      int32_t page_size);
+
+/* [host] ring_block_table -- a static block table that recycles dead rows.
+ *
+ * Request s gets the next da_ring_pages(...) physical pages from first_page
+ * on (requests in order); its logical page lp maps to its own page lp while
+ * lp < ceil(prompt_len[s] / page_size), and past that to ring slot
+ * (lp - that count) mod R.  Writing each new token's K/V row at
+ * (block_table[s][j / page_size], j % page_size) then overwrites only rows
+ * no later query of s reads, and the decode entry points, given this table,
+ * return exactly what they return on a full cache.  Entries past
+ * ceil(max_len / page_size) are set to the request's first page.
+ *   prompt_len  [host] [n_seq]
+ *   block_table [host] [n_seq][bt_stride] out, bt_stride >= ceil(max_len / page_size)
+ *   n_pages     [host] out (may be NULL): pages used by all requests
+ * Errors: DA_EINVAL (mask, sizes, null pointers, negative prompt_len, page
+ * ids past INT32_MAX), DA_ENOTSUP (causal = 0). */
+int da_ring_block_table(const da_mask* m /* [host] */, int32_t n_seq, const int32_t* prompt_len,
+                        int32_t max_len, int32_t page_size, int32_t first_page,
+                        int32_t bt_stride, int32_t* block_table, int64_t* n_pages);
+
 /* [host] Bytes of the prefill tile lists for `batch` sequences of n tokens. */
 int64_t da_prefill_tiles_bytes(int32_t batch, int32_t n);
 
