@@ -165,13 +165,16 @@ def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
                               block_table: Optional[torch.Tensor] = None,
                               scale: Optional[float] = None, out=None, lse=None,
                               want_lse: bool = False, workspace=None, count=None, idx=None,
-                              want_lists: bool = False):
+                              want_lists: bool = False, k_new=None, v_new=None):
     """Decode with the keep-set computed in the kernel from (pos, prompt_len,
     mask) -- one launch for build + attention.  q [n_q, hq, hd]; caches as in
     ``kv_cache``; seq/pos/prompt_len [n_q] int32.  With ``want_lists`` (or
     given count/idx) the lists keepset_build would write are written too.
+    k_new/v_new [n_q, hkv, hd]: the new token's K/V rows, appended to the
+    cache at pos before attention (one query per request).
     Returns (out, lse or None, count or None, idx or None)."""
-    _need_cuda("sparse_decode_attn_masked", q, k_cache, v_cache, seq, pos, prompt_len, block_table)
+    _need_cuda("sparse_decode_attn_masked", q, k_cache, v_cache, seq, pos, prompt_len, block_table,
+               k_new, v_new)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [n_q, hq, hd] tensor")
     if q.dtype not in _DTYPE or q.dtype != k_cache.dtype:
@@ -195,13 +198,20 @@ def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
     if idx is not None and (idx.dtype != torch.int32 or not idx.is_contiguous() or
                             tuple(idx.shape) != (n_q, cap) or count.dtype != torch.int32):
         raise ValueError("idx must be a contiguous int32 [n_q, cap] tensor, count int32 [n_q]")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    for t in (k_new, v_new):
+        if t is not None and (t.dtype != q.dtype or not t.is_contiguous() or
+                              tuple(t.shape) != (n_q, hkv, hd)):
+            raise ValueError("k_new and v_new must be contiguous [n_q, hkv, hd] tensors of q's dtype")
     if workspace is None:
         workspace = decode_workspace(n_q, hq, hd, cap, split, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     kv = kv_cache(k_cache, v_cache, block_table)
     check(load().da_sparse_decode_attn_masked(m, _ptr(q), _DTYPE[q.dtype], n_q, hq, hkv, hd,
                                               float(scale), kv, _ptr(seq), _ptr(pos),
-                                              _ptr(prompt_len), cap, split, _ptr(count), _ptr(idx),
+                                              _ptr(prompt_len), _ptr(k_new), _ptr(v_new),
+                                              cap, split, _ptr(count), _ptr(idx),
                                               _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                               _stream(q)),
           "da_sparse_decode_attn_masked")

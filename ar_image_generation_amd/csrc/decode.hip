@@ -51,6 +51,9 @@ struct DecodeArgs {
   int mode, W, B, G;
   int32_t* count_out;
   int32_t* idx_out;
+  // KV append (mask form): the new token's K and V rows [n_q][hkv][HD], or null
+  const void* k_new;
+  const void* v_new;
   int n_q, hq, hkv, cap, split, max_split;
   float qscale;           // scale * log2(e)
   void* out;
@@ -260,6 +263,15 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const int i = a.pos[qi];
     const int P = a.prompt[qi];
     const int sq_raw = a.seq[qi];
+    // KV append: lanes 0 .. LPR-1 carry the new token's K chunk of this kv
+    // head, lanes LPR .. 2 LPR-1 its V chunk
+    const bool appending = a.k_new != nullptr;
+    u32x4 nkv = u32x4{0u, 0u, 0u, 0u};
+    if (appending && t < 2 * LPR) {
+      const void* src = t < LPR ? a.k_new : a.v_new;
+      const int64_t off = ((int64_t)qi * a.hkv + g) * HD + c * EPL;
+      nkv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(src) + off * ES);
+    }
     __asm__ volatile("" ::: "memory");
     sq = clampi(sq_raw, 0, a.n_seq - 1);
     bt = a.block_table ? a.block_table + (int64_t)sq * a.bt_stride : nullptr;
@@ -311,7 +323,16 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     if (lists && s == 0 && t == 0) a.count_out[qi] = n;
     if (a.ws_cnt && g == 0 && s == 0 && t == 0) a.ws_cnt[qi] = n;
     cnt = n < a.cap ? n : a.cap;
-    __syncthreads();                                  // row offsets written
+    // KV append: the chunk that attends the last entry (position i itself
+    // when the list is not truncated) stores the new row at position i
+    // before the barrier below, whose release fence makes it visible to this
+    // workgroup's tile loads.  Positions outside the cache are not written.
+    if (appending && !bad && i < a.max_len && cnt > 0 && (cnt - 1) / a.split == s && t < 2 * LPR) {
+      const int64_t o = row_offset(a, bt, sq, i);
+      char* base = reinterpret_cast<char*>(const_cast<void*>(t < LPR ? a.k : a.v));
+      *reinterpret_cast<u32x4*>(base + ((int64_t)g * a.head_stride + c * EPL + o) * ES) = nkv;
+    }
+    __syncthreads();                                  // row offsets (and an appended row) written
     if (r0 >= cnt) return;
     nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
   }
@@ -679,6 +700,7 @@ extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_
                                             int32_t n_q, int32_t hq, int32_t hkv, int32_t head_dim,
                                             float scale, const da_kv_cache* kv, const int32_t* seq,
                                             const int32_t* pos, const int32_t* prompt_len,
+                                            const void* k_new, const void* v_new,
                                             int32_t cap, int32_t split, int32_t* count, int32_t* idx,
                                             void* out, float* lse, void* workspace, int64_t ws_bytes,
                                             void* stream) {
@@ -692,8 +714,13 @@ extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_
   if (n_q > 0 && (!pos || !prompt_len)) return fail(DA_EINVAL, "pos and prompt_len must be non-NULL");
   if ((count == nullptr) != (idx == nullptr))
     return fail(DA_EINVAL, "count and idx must both be given or both be NULL");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(DA_EINVAL, "k_new and v_new must both be given or both be NULL");
+  if (((uintptr_t)k_new | (uintptr_t)v_new) % 16) return fail(DA_EINVAL, "k_new and v_new must be 16-byte aligned");
   clear_error();
   if (n_q == 0) return DA_OK;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.pos = pos;
   a.prompt = prompt_len;
   a.mode = m->mode;

@@ -129,6 +129,9 @@ class DecodeBench:
                 self.seqs.append(seq + c * cfg.n_seq)
                 self.bts.append(None)
         self.out = torch.empty_like(self.q)
+        s_idx, p_idx = inp.seq.long(), inp.pos.long()
+        self.k_new = inp.k_logical[s_idx, :, p_idx].contiguous().to(dev)
+        self.v_new = inp.v_logical[s_idx, :, p_idx].contiguous().to(dev)
         self.ws = {}
         self.splits = {mode: (cfg.dense_split if mode == da.DENSE else self.split)
                        for mode in self.lists}
@@ -149,14 +152,17 @@ class DecodeBench:
                                    split=self.splits[mode], block_table=self.bts[c],
                                    out=self.out, workspace=self.ws[mode])
 
-    def decode_masked(self, mode, c):
+    def decode_masked(self, mode, c, append=False):
         """Keep-set build and attention in one launch; the lists are written
-        too (the same count/idx keepset_build writes)."""
+        too (the same count/idx keepset_build writes).  append=True also
+        writes each query's own K/V row (the values already there)."""
         m, cap, count, idx = self.lists[mode]
+        kn, vn = (self.k_new, self.v_new) if append else (None, None)
         self.da.sparse_decode_attn_masked(m, self.q, self.k, self.v, self.seqs[c], self.pos,
                                           self.prompt, cap=cap, split=self.splits[mode],
                                           block_table=self.bts[c], out=self.out,
-                                          workspace=self.ws[mode], count=count, idx=idx)
+                                          workspace=self.ws[mode], count=count, idx=idx,
+                                          k_new=kn, v_new=vn)
 
     def kept_bytes(self, mode):
         return self.kept[mode] * kv_bytes_per_key(self.cfg)
@@ -164,8 +170,8 @@ class DecodeBench:
     def step(self, mode, c, path):
         """One step: 'fused' = decode_masked; 'lists' = keepset_build then
         sparse_decode_attn; 'decode' = sparse_decode_attn on built lists."""
-        if path == "fused":
-            self.decode_masked(mode, c)
+        if path in ("fused", "append"):
+            self.decode_masked(mode, c, append=path == "append")
             return
         if path == "lists":
             self.build(mode)
@@ -176,7 +182,7 @@ class DecodeBench:
         replays it once untimed and once timed (events on the capture
         stream).  Returns microseconds per step.  with_build=False captures
         decode launches only (the decode kernel's average duration); `path`
-        overrides with 'fused', 'lists' or 'decode'."""
+        overrides with 'fused', 'append' (fused with KV append), 'lists' or 'decode'."""
         torch = self.torch
         n = self.n_copies if rotate else 1
         path = path or ("lists" if with_build else "decode")
@@ -661,11 +667,13 @@ def main():
     us_step_warm = b.time_graph(mode, K, W, rotate=False, path="fused")
     # the same step as two launches, and its decode kernel alone
     us_step_l = b.time_graph(mode, K, W, path="lists")
+    us_step_a = b.time_graph(mode, K, W, path="append")
     us_dec = b.time_graph(mode, K, W, path="decode")
     us_step_d = b.time_graph(da.DENSE, K, W, path="fused")
     us_dec_d = b.time_graph(da.DENSE, K, W, path="decode")
     us_eager = b.time_eager(mode, K, W)
     log(f"[bench] {cfg.name} sparse: fused step {us_step:.2f} us cold / {us_step_warm:.2f} us warm; "
+        f"with KV append {us_step_a:.2f} us; "
         f"list path {us_step_l:.2f} us/step (decode kernel {us_dec:.2f} us), {us_eager:.2f} us/step "
         f"eager; dense fused {us_step_d:.2f} us/step, dense decode {us_dec_d:.2f} us")
 
@@ -777,6 +785,8 @@ def main():
                       "decode_us": round(us_dec, 3),
                       "decode_kept_GBps": round(kept / (us_dec * 1e-6) / 1e9, 1),
                       "eager_us_per_step": round(us_eager, 2)},
+        "with_kv_append": {"us_per_step": round(us_step_a, 2),
+                           "tokens_per_s": round(b.n_q / (us_step_a * 1e-6), 1)},
         "warm": {"us_per_step": round(us_step_warm, 2),
                  "kept_GBps": round(kept / (us_step_warm * 1e-6) / 1e9, 1)},
         "dense": {"us_per_step": round(us_step_d, 2), "decode_us": round(us_dec_d, 2),

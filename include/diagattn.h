@@ -202,18 +202,27 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
  *   count, idx  optional outputs (both or neither): the lists exactly as
  *          da_keepset_build writes them (count[q] the true size; idx[q*cap+r]
  *          for r < min(count[q], cap)), for callers that reuse them
+ *   k_new, v_new optional inputs (both or neither) [n_q][hkv][head_dim] in
+ *          `dtype`, 16-byte aligned: KV append.  The row of each query's own
+ *          position pos[q] is written into the cache (kv->k, kv->v, which must
+ *          then be writable) before it is read, so the step attends to the new
+ *          token's key and value.  Precondition: no query of the call reads a
+ *          row another query of the call appends (e.g. one query per request);
+ *          positions outside [0, kv->max_len) are not written.
  *   other arguments as for da_sparse_decode_attn (cap bounds the entries a
  *          query attends to and sizes the chunk grid with `split`).
  * Device data: pos[q] < 0 or prompt_len[q] < 0 gives count 0 and no output
  * written for that query; positions and requests are clamped into the
  * descriptor's extents.
  * Errors: as da_sparse_decode_attn, plus DA_EINVAL for an invalid mask, null
- * pos/prompt_len, or only one of count/idx given, DA_ENOTSUP for causal = 0. */
+ * pos/prompt_len, only one of count/idx or of k_new/v_new given, or
+ * misaligned k_new/v_new; DA_ENOTSUP for causal = 0. */
 int da_sparse_decode_attn_masked(const da_mask* m /* [host] */, const void* q,
                                  da_dtype dtype, int32_t n_q, int32_t hq, int32_t hkv,
                                  int32_t head_dim, float scale,
                                  const da_kv_cache* kv /* [host] */, const int32_t* seq,
                                  const int32_t* pos, const int32_t* prompt_len,
+                                 const void* k_new, const void* v_new,
                                  int32_t cap, int32_t split, int32_t* count, int32_t* idx,
                                  void* out, float* lse, void* workspace, int64_t ws_bytes,
                                  void* stream);

@@ -153,3 +153,42 @@ def test_without_lists_same_output():
     torch.cuda.synchronize()
     assert c2 is None and c1 is not None
     assert torch.equal(o1.cpu(), o2.cpu())
+
+
+@pytest.mark.parametrize("name,n_seq,split", [("llamagen_b16", 4, 4096), ("llamagen_b16", 4, 32),
+                                              ("paged_b128", 5, 4096), ("paged_b128", 5, 48)])
+def test_kv_append(name, n_seq, split):
+    """KV append: on a cache missing each query's own row, the step with
+    k_new/v_new equals the step on the complete cache, and leaves the cache
+    complete (one query per request)."""
+    cfg = wl.small_decode(name, n_seq=n_seq)
+    inp = wl.decode_inputs(cfg)
+    k_full, v_full, bt = caches(inp)
+    s_idx, p_idx = inp.seq.long(), inp.pos.long()
+    k_new = inp.k_logical[s_idx, :, p_idx].contiguous().to(dev())      # [n_q, hkv, hd]
+    v_new = inp.v_logical[s_idx, :, p_idx].contiguous().to(dev())
+    if bt is None:
+        rows = (s_idx.to(dev()), slice(None), p_idx.to(dev()))
+    else:
+        ps = k_full.shape[2]
+        pages = bt[s_idx.to(dev()), (p_idx // ps).to(dev())].long()
+        rows = (pages, slice(None), (p_idx % ps).to(dev()))
+    q, seq, pos, prompt = (inp.q.to(dev()), inp.seq.to(dev()), inp.pos.to(dev()),
+                           inp.prompt_len.to(dev()))
+    for mode in sorted(set(cfg.modes) | {O.DENSE}):
+        m = da.mask(mode, cfg.W, cfg.B, cfg.G)
+        cap = da.keep_cap(m, int(inp.pos.max()), int(inp.prompt_len.max()))
+        k_miss, v_miss = k_full.clone(), v_full.clone()
+        k_miss[rows] = 0
+        v_miss[rows] = 0
+        assert not torch.equal(k_miss, k_full)
+        ref, ref_lse, _, _ = da.sparse_decode_attn_masked(m, q, k_full, v_full, seq, pos, prompt,
+                                                          cap=cap, split=split, block_table=bt,
+                                                          want_lse=True)
+        got, got_lse, _, _ = da.sparse_decode_attn_masked(m, q, k_miss, v_miss, seq, pos, prompt,
+                                                          cap=cap, split=split, block_table=bt,
+                                                          want_lse=True, k_new=k_new, v_new=v_new)
+        torch.cuda.synchronize()
+        assert torch.equal(got.cpu(), ref.cpu()), mode
+        assert torch.equal(got_lse.cpu(), ref_lse.cpu()), mode
+        assert torch.equal(k_miss, k_full) and torch.equal(v_miss, v_full), mode
