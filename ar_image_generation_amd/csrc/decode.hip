@@ -278,6 +278,18 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     off0 = bt ? (int64_t)clampi(bt[0], 0, a.n_pages - 1) * a.page_stride
               : (int64_t)sq * a.page_stride;
     const bool bad = i < 0 || P < 0;
+    // KV append: lanes 0 .. 2 LPR-1 store the new K / V row at position i
+    // (positions outside the cache are not written)
+    auto store_new_row = [&]() {
+      if (t < 2 * LPR) {
+        const int64_t o = row_offset(a, bt, sq, i);
+        char* base = reinterpret_cast<char*>(const_cast<void*>(t < LPR ? a.k : a.v));
+        *reinterpret_cast<u32x4*>(base + ((int64_t)g * a.head_stride + c * EPL + o) * ES) = nkv;
+      }
+    };
+    // one chunk per query: this workgroup is the only reader of the row, so
+    // it stores now and the store completes under the keep-set scan
+    if (appending && a.max_split == 1 && !bad && i < a.max_len) store_new_row();
     const int L = i + 1;
     int Pc = 0, wlo = 1, whi = 0;
     if (!bad) {
@@ -323,15 +335,12 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     if (lists && s == 0 && t == 0) a.count_out[qi] = n;
     if (a.ws_cnt && g == 0 && s == 0 && t == 0) a.ws_cnt[qi] = n;
     cnt = n < a.cap ? n : a.cap;
-    // KV append: the chunk that attends the last entry (position i itself
-    // when the list is not truncated) stores the new row at position i
+    // KV append, several chunks: the chunk that attends the last entry
+    // (position i itself when the list is not truncated) stores the new row
     // before the barrier below, whose release fence makes it visible to this
-    // workgroup's tile loads.  Positions outside the cache are not written.
-    if (appending && !bad && i < a.max_len && cnt > 0 && (cnt - 1) / a.split == s && t < 2 * LPR) {
-      const int64_t o = row_offset(a, bt, sq, i);
-      char* base = reinterpret_cast<char*>(const_cast<void*>(t < LPR ? a.k : a.v));
-      *reinterpret_cast<u32x4*>(base + ((int64_t)g * a.head_stride + c * EPL + o) * ES) = nkv;
-    }
+    // workgroup's tile loads.
+    if (appending && a.max_split > 1 && !bad && i < a.max_len && cnt > 0 && (cnt - 1) / a.split == s)
+      store_new_row();
     __syncthreads();                                  // row offsets (and an appended row) written
     if (r0 >= cnt) return;
     nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
