@@ -370,6 +370,72 @@ DECODE_SRC = [os.path.join(ROOT, "ar_image_generation_amd", "csrc", f)
 PROBE_BYTES = 256 << 20
 
 
+def graph_us(torch, fn, n, steps, warmup):
+    """Microseconds per call of fn(c) for c cycling over n copies: `warmup`
+    eager calls, then `steps` calls captured in one HIP graph, replayed once
+    untimed and once timed with events on the capture stream."""
+    for w in range(warmup):
+        fn(w % n)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(steps):
+            fn((warmup + s) % n)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    del g
+    return us
+
+
+def mask_sweep(b, steps, warmup, w_rows=(1, 2, 3, 6), bands=(0, 1, 2, 4)):
+    """Row-diagonal masks over a B x W grid at the benchmark shape: the
+    one-launch step's time and kept bytes, and the share of the dense
+    attention mass each keep-set captures, exp(lse_sparse - lse_dense), per
+    (query, head).  The inputs are synthetic (random queries), so the share
+    is a proxy of the quality side, not image quality."""
+    torch, da = b.torch, b.da
+    cfg = b.cfg
+    maxpos, maxp = int(b.inp.pos.max()), int(b.inp.prompt_len.max())
+    dense = da.mask(da.DENSE, 0, 0, 1)
+    capd = da.keep_cap(dense, maxpos, maxp)
+    _, lse_d, _, _ = da.sparse_decode_attn_masked(
+        dense, b.q, b.k, b.v, b.seqs[0], b.pos, b.prompt, cap=capd, split=cfg.dense_split,
+        block_table=b.bts[0], want_lse=True)
+    rows = []
+    for wr in w_rows:
+        for bw in bands:
+            m = da.mask(da.ROWDIAG, wr * cfg.G, bw, cfg.G)
+            cap = da.keep_cap(m, maxpos, maxp)
+            split = max(cap, 1)
+            out = torch.empty_like(b.q)
+            lse = torch.empty((b.n_q, cfg.hq), dtype=torch.float32, device=b.q.device)
+
+            def run(c, m=m, cap=cap, split=split, out=out, lse=lse):
+                da.sparse_decode_attn_masked(m, b.q, b.k, b.v, b.seqs[c], b.pos, b.prompt, cap=cap,
+                                             split=split, block_table=b.bts[c], out=out, lse=lse)
+            us = graph_us(torch, run, b.n_copies, steps, warmup)
+            run(0)
+            torch.cuda.synchronize()
+            share = torch.exp(lse - lse_d)
+            kept = sum(da.keep_count(m, int(p), int(P)) for p, P in zip(*b.hosts))
+            kb = kept * kv_bytes_per_key(cfg)
+            rows.append({"W_rows": wr, "W": wr * cfg.G, "B": bw,
+                         "kept_per_query": round(kept / b.n_q, 2), "us_per_step": round(us, 2),
+                         "kept_GBps": round(kb / (us * 1e-6) / 1e9, 1),
+                         "mass_share_mean": round(share.mean().item(), 4),
+                         "mass_share_min": round(share.min().item(), 4)})
+            log(f"[bench] sweep W={wr}x{cfg.G} B={bw}: {kept / b.n_q:.0f} kept/query, {us:.2f} us, "
+                f"mass share {share.mean().item():.3f} (min {share.min().item():.3f})")
+    return rows
+
+
 def burn_in(bufs, seconds):
     """Streams the given device tensors until `seconds` have passed, so the
     memory and core clocks have left their idle states before anything is
@@ -685,6 +751,8 @@ def main():
     value = b.n_q / (us_step * 1e-6)
     traffic = traffic_from_profile(cfg.name)
 
+    sweep = mask_sweep(b, K, W) if not args.no_extra else None
+
     # keep-set-aware KV residency: the same step through a ring block table
     residency = {}
     if not args.no_extra:
@@ -795,6 +863,7 @@ def main():
                   "speedup_decode": round(us_dec_d / us_dec, 3)},
         "extra": extra,
         "kv_residency": residency,
+        "mask_sweep": sweep,
         "prefill": prefill,
     }
     print(json.dumps(line), flush=True)

@@ -192,3 +192,34 @@ def test_kv_append(name, n_seq, split):
         assert torch.equal(got.cpu(), ref.cpu()), mode
         assert torch.equal(got_lse.cpu(), ref_lse.cpu()), mode
         assert torch.equal(k_miss, k_full) and torch.equal(v_miss, v_full), mode
+
+
+def test_mass_share_from_lse_matches_direct_softmax():
+    """exp(lse_sparse - lse_dense) is the share of the dense softmax mass on
+    the keep-set; compared with that share summed directly in fp64 from the
+    oracle's keep-sets (relative 1e-3: two LSEs within 1e-4 each, plus bf16)."""
+    cfg = wl.small_decode("llamagen_b16", n_seq=3)
+    inp = wl.decode_inputs(cfg)
+    k, v, bt = caches(inp)
+    args = (inp.q.to(dev()), k, v, inp.seq.to(dev()), inp.pos.to(dev()), inp.prompt_len.to(dev()))
+    dense = da.mask(O.DENSE, 0, 0, 1)
+    _, lse_d, _, _ = da.sparse_decode_attn_masked(dense, *args, cap=int(inp.pos.max()) + 1,
+                                                  split=4096, block_table=bt, want_lse=True)
+    q = inp.q.double().numpy()
+    K = inp.k_logical.double().numpy()
+    for W, B in [(32, 0), (96, 2), (192, 4)]:
+        m = da.mask(O.ROWDIAG, W, B, cfg.G)
+        cap = da.keep_cap(m, int(inp.pos.max()), int(inp.prompt_len.max()))
+        _, lse_s, _, _ = da.sparse_decode_attn_masked(m, *args, cap=cap, split=4096, block_table=bt,
+                                                      want_lse=True)
+        torch.cuda.synchronize()
+        share = torch.exp(lse_s - lse_d).double().cpu().numpy()
+        for qi in range(inp.n_q):
+            i, P, s = int(inp.pos[qi]), int(inp.prompt_len[qi]), int(inp.seq[qi])
+            kept = O.keepset(i, P=P, W=W, B=B, G=cfg.G, mode=O.ROWDIAG)
+            for h in range(cfg.hq):
+                g = h // (cfg.hq // cfg.hkv)
+                sc = K[s, g, : i + 1] @ q[qi, h] / np.sqrt(cfg.hd)
+                w = np.exp(sc - sc.max())
+                want = w[kept].sum() / w.sum()
+                assert abs(share[qi, h] - want) <= 1e-3 * want, (W, B, qi, h, share[qi, h], want)
