@@ -23,6 +23,13 @@
 // needs agent-scope fences, which write back and invalidate the whole L2 of
 // the XCD on this part: measured far slower than a second launch.)
 //
+// Mask form (MASKED): instead of reading lists, each workgroup builds the
+// entries of its chunk from the query's position, prompt length and the
+// mask with the list builder's rule and order (prompt entries directly, the
+// window by a ballot scan), so keep-set build and attention are one launch;
+// the lists can be written out as well, and the new token's K/V rows can be
+// appended to the cache at its position before they are read.
+//
 // Every index read from device memory (request, position, page) is clamped
 // into the cache extents the host passes, so no list content can make the
 // kernel read outside the cache.
@@ -186,7 +193,6 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int qi = qg / a.hkv;
   const int g = qg % a.hkv;
   const int r0 = s * a.split;
-  const int32_t* myidx = a.idx + (int64_t)qi * a.cap + r0;
   const int lim = a.cap - r0 < a.split ? a.cap - r0 : a.split;   // >= 1
 
   // ---- stage 0: query slices, list entries, count and request in one
@@ -202,6 +208,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int32_t* bt;
   int64_t off0;
   if constexpr (!MASKED) {
+    const int32_t* myidx = a.idx + (int64_t)qi * a.cap + r0;
     int jj[IPT];
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {

@@ -5,8 +5,13 @@
 One step = keep-set build + sparse decode attention (plus the chunk merge
 when a keep-set spans several chunks) for one batch of the LlamaGen-like
 decode workload: 16 requests x 32 heads, head_dim 128, bf16 KV, prompt 120
-tokens, 32x32 raster grid, W = 3 rows, B = 2, row-diagonal mode.  Inputs are
-seeded synthetic tensors, resident in HBM before timing starts.
+tokens, 32x32 raster grid, W = 3 rows, B = 2, row-diagonal mode -- as one
+launch (sparse_decode_attn_masked, which also writes the keep-set lists).
+The same step as two launches (keepset_build, sparse_decode_attn) is
+reported beside it, with the dense run at the same shape, the other decode
+workloads, a streaming-read probe of the same byte count, a KV append run,
+the ring-cache (KV residency) run, a B x W mask sweep and the band prefill.
+Inputs are seeded synthetic tensors, resident in HBM before timing starts.
 
 Cold-cache timing: the KV cache is replicated on the device and step k reads
 copy k mod n, with n chosen so that at least 1 GiB of other kept rows is
@@ -688,7 +693,7 @@ def main():
     ap.add_argument("--workload", default="llamagen_b16")
     ap.add_argument("--split", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the other decode workloads")
+    ap.add_argument("--no-extra", action="store_true", help="skip everything but the headline step, its dense run and the probe")
     ap.add_argument("--profile-run", action="store_true",
                     help="run only the timed decode launches and one probe (for rocprofv3)")
     ap.add_argument("--prefill", action="store_true",
