@@ -4,8 +4,9 @@
 // listed keys).  Each K/V row (head_dim elements, 128-512 bytes) is read by
 // LPR = row_bytes / 16 consecutive lanes with one 16-byte load each, so one
 // wave instruction moves 1 KiB and the rows of a run are contiguous in
-// memory.  Rows are taken in tiles of NP passes (NP * 256 / LPR rows); two
-// tiles are in flight while the older one is reduced.  Before the first
+// memory.  Rows are taken in tiles of NP passes (NP * 256 / LPR rows); a
+// chunk of at most three tiles has all of them in flight at once, longer
+// chunks keep two in flight while the older one is reduced.  Before the first
 // tile, every index of the chunk, then (paged caches) every block-table
 // entry, is read in one round trip each and turned into a row offset in LDS,
 // so no K/V load waits on more than the loads issued before it.  The kernel
@@ -414,13 +415,25 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   };
 
   TL b0, b1;
-  b0.load(kb, vb, rowoff, off0, 0, rsub, nrows);
-  for (int tt = 0; tt < nt; tt += 2) {
-    b1.load(kb, vb, rowoff, off0, tt + 1, rsub, nrows);
-    process(b0, tt);
-    if (tt + 1 >= nt) break;
-    b0.load(kb, vb, rowoff, off0, tt + 2, rsub, nrows);
-    process(b1, tt + 1);
+  if (nt <= 3) {
+    // short chunk: every tile in flight at once, none loaded past the end
+    // (the two-buffer loop below always issues one tile of lookahead)
+    TL b2;
+    b0.load(kb, vb, rowoff, off0, 0, rsub, nrows);
+    b1.load(kb, vb, rowoff, off0, 1, rsub, nrows);
+    b2.load(kb, vb, rowoff, off0, 2, rsub, nrows);
+    process(b0, 0);
+    if (nt > 1) process(b1, 1);
+    if (nt > 2) process(b2, 2);
+  } else {
+    b0.load(kb, vb, rowoff, off0, 0, rsub, nrows);
+    for (int tt = 0; tt < nt; tt += 2) {
+      b1.load(kb, vb, rowoff, off0, tt + 1, rsub, nrows);
+      process(b0, tt);
+      if (tt + 1 >= nt) break;
+      b0.load(kb, vb, rowoff, off0, tt + 2, rsub, nrows);
+      process(b1, tt + 1);
+    }
   }
 
   // ---- combine the row slots of each wave (lanes with the same chunk c)
