@@ -223,3 +223,28 @@ def test_mass_share_from_lse_matches_direct_softmax():
                 w = np.exp(sc - sc.max())
                 want = w[kept].sum() / w.sum()
                 assert abs(share[qi, h] - want) <= 1e-3 * want, (W, B, qi, h, share[qi, h], want)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_configurations(seed):
+    """Seeded random shapes and masks (dtype, head size, GQA ratio, paged or
+    contiguous cache, grid, window, band, prompt range, split): the mask
+    path against the oracle, and bitwise against the list path."""
+    rng = np.random.default_rng(500 + seed)
+    hd = int(rng.choice([64, 128]))
+    hkv = int(rng.choice([1, 2]))
+    hq = hkv * int(rng.choice([1, 2, 4, 8]))
+    pmin = int(rng.integers(0, 60))
+    cfg = wl.small_decode(
+        "paged_b128", n_seq=int(rng.integers(1, 5)), hq=hq, hkv=hkv, hd=hd,
+        dtype=str(rng.choice(["f32", "bf16"])), prompt=(pmin, pmin + int(rng.integers(0, 40))),
+        G=int(rng.integers(1, 40)), W=int(rng.integers(0, 200)), B=int(rng.integers(0, 8)),
+        modes=(O.BAND, O.ROWDIAG), pos_rule="image", page_size=int(rng.choice([0, 4, 16])),
+        kv_gen="normal", seed=700 + seed)
+    inp = wl.decode_inputs(cfg)
+    split = int(rng.choice([16, 48, 4096]))
+    for mode in (O.DENSE, O.BAND, O.ROWDIAG):
+        a, b, cap = both_paths(inp, mode, split)
+        assert_same(a, b, cap)
+        ref_o, ref_l = run_oracle(inp, mode)
+        assert_close(b[0], b[1], ref_o, ref_l, cfg.dtype)

@@ -120,3 +120,26 @@ def test_prefill_row_matches_decode_at_that_position():
     torch.cuda.synchronize()
     diff = (dec.cpu().float().permute(1, 0, 2) - out[0].float()).abs().max().item()
     assert diff <= ATOL
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_masks_and_shapes(seed):
+    """Seeded random masks (any mode, overlapping bands, G = 1, W = 0,
+    prompts longer than the sequence), ragged lengths, both head sizes and
+    GQA ratios: every row against the oracle."""
+    rng = np.random.default_rng(100 + seed)
+    mode = int(rng.choice([O.DENSE, O.BAND, O.ROWDIAG]))
+    hd = int(rng.choice([64, 128]))
+    kvh, rep = int(rng.choice([1, 2])), int(rng.choice([1, 2]))
+    heads = kvh * rep
+    n = int(rng.integers(1, 600))
+    batch = int(rng.integers(1, 3))
+    G = int(rng.integers(1, 80))
+    W, B = int(rng.integers(0, 300)), int(rng.integers(0, 12))
+    prompt = [int(rng.integers(0, n + 6)) for _ in range(batch)]
+    q = randn((batch, heads, n, hd), 200 + seed)
+    k = randn((batch, kvh, n, hd), 300 + seed)
+    v = randn((batch, kvh, n, hd), 400 + seed)
+    out, lse = run(q, k, v, prompt, mode, W, B, G)
+    rows = [(b, h, i) for b in range(batch) for h in range(heads) for i in range(n)]
+    check(out, lse, oracle_rows(q, k, v, prompt, mode, W, B, G, rows))
