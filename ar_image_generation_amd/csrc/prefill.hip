@@ -4,7 +4,8 @@
 // Workgroup = 8 waves = 256 query rows of one (batch, head); each wave owns
 // two blocks of 16 rows.  The 64-key tiles that hold a kept pair (listed
 // once per query tile by prefill_tiles_kernel) stream K and V into a ring of
-// LDS stages by direct global->LDS copies, three tiles ahead.  Scores are
+// four LDS stages by direct global->LDS copies; the loop takes them in
+// steps of two tiles, fetching the next pair while it computes.  Scores are
 // computed transposed, S^T = K Q^T (A = K from LDS, B = Q^T from
 // registers), so that the MFMA result gives every lane one query row and
 // four keys of each 16-key block.  That lane-per-row layout is kept for the
@@ -288,9 +289,8 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   }
   __syncthreads();
 
-#pragma unroll
-  for (int k = 0; k < NS - 1; ++k)
-    if (k < cnt) issue(tl[k].x, k);
+  issue(tl[0].x, 0);
+  if (cnt > 1) issue(tl[1].x, 1);
 
   if constexpr (MODE == DA_MODE_ROWDIAG) {
     // band centres of residue r within reach of bits 0..63: r - kG for
@@ -335,13 +335,38 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   const int vt_sub = (lr & 3);
   const int my_i0 = wi0 + lr;          // this lane's row in block 0 (block rb adds 16 rb)
 
-  // S^T = K Q^T for every 16-key block of one staged tile (A = K from LDS,
-  // shared by the RB row blocks)
-  auto scores = [&](const uint16_t* ksm, f32x4 (&sc)[RB][4]) {
+  // Masks: a 64-bit keep word per row over the keys of the tile whose first
+  // key is j0 -- causal bits, prompt bits and the window rule -- applied to
+  // that tile's four 16-key score blocks (half 0 or 1 of a step): each score
+  // the lane holds (key 16kq + 4lg + r) keeps its bit or becomes -inf.
+  auto apply_mask = [&](f32x4 (&sc)[RB][8], int half, int j0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const int x = my_i0 + 16 * rb - j0;
+      uint64_t win;
+      if constexpr (MODE == DA_MODE_ROWDIAG) win = bp[mod_g(x, G, a.inv_g)] & bit_range(x - W, x);
+      else if constexpr (MODE == DA_MODE_BAND) win = bit_range(x - (Bw < W ? Bw : W), x);
+      else win = ~uint64_t(0);
+      const uint64_t keep = (win | bit_range(0, P - j0 - 1)) & bit_range(0, x);
+      const uint64_t sh = keep >> (4 * lg);
+      const uint32_t wd[2] = {(uint32_t)sh, (uint32_t)(sh >> 32)};
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int32_t m = (int32_t)(wd[kq >> 1] << (31 - (16 * (kq & 1) + r))) >> 31;
+          sc[rb][4 * half + kq][r] =
+              __int_as_float((__float_as_int(sc[rb][4 * half + kq][r]) & m) | (~m & (int32_t)0xff800000));
+        }
+    }
+  };
+  // S^T = K Q^T for the four 16-key blocks of one staged tile (A = K from
+  // LDS, shared by the RB row blocks), into half `half` of a step's scores
+  auto scores_into = [&](const uint16_t* ksm, f32x4 (&sc)[RB][8], int half) {
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sc[rb][kq] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < RB; ++rb) sc[rb][4 * half + kq] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int row = 16 * kq + lr;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -349,80 +374,55 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ksm + row * HD + pos * 8);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          sc[rb][kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][kq], 0, 0, 0);
+          sc[rb][4 * half + kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][4 * half + kq], 0, 0, 0);
       }
     }
   };
 
-  // Software pipeline over the listed tiles.  Iteration idx computes the
-  // scores of tile idx+1 while it runs the softmax and P.V of tile idx, so
-  // the matrix cores and the vector ALUs work at the same time.  Stages:
-  // tile t lives in stage t % NS; at the top of iteration idx tile idx+1
-  // must have landed (tile idx+2 may still be in flight) and everyone must
-  // be done with iteration idx-1, whose stage receives tile idx+3.
-  __syncthreads();                     // first tiles landed, band pattern written
-  f32x4 sc_cur[RB][4];
-  scores(ring, sc_cur);
-  for (int idx = 0; idx < cnt; ++idx) {
-    if (idx + 2 < cnt) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DPW));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");   // no ring read moves above the wait
-    if (idx + NS - 1 < cnt) issue(tl[idx + NS - 1].x, (idx + NS - 1) % NS);
-
-    const int4 e = tl[idx];
-    const uint64_t full64 = (uint64_t)(uint32_t)e.y | ((uint64_t)(uint32_t)e.z << 32);
-    const unsigned fullw = (unsigned)(full64 >> (wave * 8)) & 0xffu;
-    const int j0 = e.x * BN;
-    const uint16_t* vsm = ring + (idx % NS) * 2 * TILE + TILE;
-
-    // scores of the next tile (its stage is resident; past the end this
-    // reads a stale stage and the result is never used)
-    f32x4 sc_nxt[RB][4];
-    const uint16_t* knext = ring + ((idx + 1) % NS) * 2 * TILE;
-
-    scores(knext, sc_nxt);
-
-    // ---- masks of tile idx (skipped when every block of this wave is
-    // wholly kept): a 64-bit keep word per row over the tile's keys --
-    // causal bits, prompt bits, and the window rule -- then each score the
-    // lane holds (key 16kq + 4lg + r) keeps its bits or becomes -inf
-    if (fullw != 0xffu) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int x = my_i0 + 16 * rb - j0;           // row minus the tile's first key
-        uint64_t win;
-        if constexpr (MODE == DA_MODE_ROWDIAG) win = bp[mod_g(x, G, a.inv_g)] & bit_range(x - W, x);
-        else if constexpr (MODE == DA_MODE_BAND) win = bit_range(x - (Bw < W ? Bw : W), x);
-        else win = ~uint64_t(0);
-        const uint64_t keep = (win | bit_range(0, P - j0 - 1)) & bit_range(0, x);
-        const uint64_t sh = keep >> (4 * lg);
-        const uint32_t wd[2] = {(uint32_t)sh, (uint32_t)(sh >> 32)};
-#pragma unroll
-        for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int32_t m = (int32_t)(wd[kq >> 1] << (31 - (16 * (kq & 1) + r))) >> 31;
-            sc_cur[rb][kq][r] = __int_as_float((__float_as_int(sc_cur[rb][kq][r]) & m) |
-                                               (~m & (int32_t)0xff800000));
-          }
-      }
+  // Steps of two listed tiles (128 keys): one wait and one barrier per step,
+  // one max / rescale, P.V over four 32-key chunks.  Tile t lives in stage
+  // t % NS.  At the top of step idx tiles idx and idx+1 have landed and all
+  // waves are done with step idx-2, whose stages then receive tiles idx+2
+  // and idx+3 -- fetched while this step computes.
+  __syncthreads();                     // tiles 0 and 1 landed, band pattern written
+  for (int idx = 0; idx < cnt; idx += 2) {
+    if (idx > 0) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // tiles idx, idx+1 (this wave's part)
+      __builtin_amdgcn_s_barrier();               // everyone's part; step idx-2 done
+      __asm__ volatile("" ::: "memory");
     }
+    if (idx + 2 < cnt) issue(tl[idx + 2].x, (idx + 2) % NS);
+    if (idx + 3 < cnt) issue(tl[idx + 3].x, (idx + 3) % NS);
+    const bool two = idx + 1 < cnt;
+    const int4 e0 = tl[idx];
+    const int4 e1 = tl[two ? idx + 1 : idx];
+    const unsigned full0 = (unsigned)((((uint64_t)(uint32_t)e0.y | ((uint64_t)(uint32_t)e0.z << 32)) >> (wave * 8)) & 0xffu);
+    const unsigned full1 = (unsigned)((((uint64_t)(uint32_t)e1.y | ((uint64_t)(uint32_t)e1.z << 32)) >> (wave * 8)) & 0xffu);
+    const uint16_t* st0 = ring + (idx % NS) * 2 * TILE;
+    const uint16_t* st1 = ring + ((idx + 1) % NS) * 2 * TILE;
 
-    // ---- online softmax (lazy reference max) and P^T operands.  The tile
-    // maxima of both row blocks come first and share one (rare) rescale
-    // branch, so that every exponential lands in the same block as the P.V
-    // products below.  The reference max only moves when a row's max grows
-    // by more than 2^8 (p <= 256 is exact enough in bf16 and fp32).
+    f32x4 sc[RB][8];
+    scores_into(st0, sc, 0);
+    if (two) {
+      scores_into(st1, sc, 1);
+    } else {                           // odd count: the second half is empty
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kq = 4; kq < 8; ++kq) sc[rb][kq] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    }
+    if (full0 != 0xffu) apply_mask(sc, 0, e0.x * BN);
+    if (two && full1 != 0xffu) apply_mask(sc, 1, e1.x * BN);
+
     float mts[RB];
     bool grow = false;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       float mt = -INFINITY;
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
+      for (int kq = 0; kq < 8; ++kq)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc_cur[rb][kq][r]);
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[rb][kq][r]);
       mts[rb] = max_over_row_groups(mt) * a.qscale;
       grow = grow || mts[rb] > mq[rb] + 8.f;
     }
@@ -439,48 +439,42 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
         mq[rb] = mn;
       }
     }
-    bf16x8 pb[RB][2];
+    bf16x8 pb[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float mref = mq[rb] == -INFINITY ? 0.f : mq[rb];
-      // slot e of 32-key chunk cc is key 32cc + (e/4)*16 + 4lg + e%4
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
+      for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc_cur[rb][2 * cc + e / 4][e % 4], a.qscale, -mref));
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[rb][2 * cc + e / 4][e % 4], a.qscale, -mref));
           ls[rb] += p;
           pb[rb][cc][e] = (__bf16)p;
         }
-      }
     }
-
-    // ---- O^T += V^T P^T: A = V^T by transpose reads of row-major V; lane L
-    // of group g addresses key 4g + L/4 of a 16-key half, dims
-    // 16nb + 4(L%4) .. +4, and receives keys 4g + 0..3 at dim 16nb + L
+    auto pv = [&](const uint16_t* vsm, int cbase) {
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
+      for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        typedef short v4i16 __attribute__((ext_vector_type(4)));
-        const int chunk = 2 * nb + (vt_sub >> 1);
-        const int r_lo = 32 * cc + vt_row, r_hi = r_lo + 16;
-        const uint16_t* plo = vsm + r_lo * HD + ((chunk ^ swz<CPR>(r_lo)) * 8) + (vt_sub & 1) * 4;
-        const uint16_t* phi = vsm + r_hi * HD + ((chunk ^ swz<CPR>(r_hi)) * 8) + (vt_sub & 1) * 4;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
-        typedef short v8i16 __attribute__((ext_vector_type(8)));
-        const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+        for (int nb = 0; nb < NB; ++nb) {
+          typedef short v4i16 __attribute__((ext_vector_type(4)));
+          const int chunk = 2 * nb + (vt_sub >> 1);
+          const int r_lo = 32 * ch + vt_row, r_hi = r_lo + 16;
+          const uint16_t* plo = vsm + r_lo * HD + ((chunk ^ swz<CPR>(r_lo)) * 8) + (vt_sub & 1) * 4;
+          const uint16_t* phi = vsm + r_hi * HD + ((chunk ^ swz<CPR>(r_hi)) * 8) + (vt_sub & 1) * 4;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
+          typedef short v8i16 __attribute__((ext_vector_type(8)));
+          const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][cc], o[rb][nb], 0, 0, 0);
+          for (int rb = 0; rb < RB; ++rb)
+            o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][cbase + ch], o[rb][nb], 0, 0, 0);
+        }
       }
-    }
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq) sc_cur[rb][kq] = sc_nxt[rb][kq];
+    };
+    pv(st0 + TILE, 0);
+    if (two) pv(st1 + TILE, 2);
   }
 
   // ---- normalise and store: lane holds row wi0+16rb+lr, dims 16nb + 4lg + r
