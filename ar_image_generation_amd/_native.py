@@ -50,7 +50,7 @@ SIGNATURES = {
     "da_sparse_decode_attn_masked": (ctypes.c_int, [ctypes.POINTER(DaMask), c_vp, ctypes.c_int, c_i32,
                                                     c_i32, c_i32, c_i32, c_f32,
                                                     ctypes.POINTER(DaKvCache), c_vp, c_vp, c_vp,
-                                                    c_vp, c_vp,
+                                                    c_vp, c_vp, c_vp,
                                                     c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp,
                                                     c_i64, c_vp]),
 }

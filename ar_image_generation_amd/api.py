@@ -165,16 +165,17 @@ def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
                               block_table: Optional[torch.Tensor] = None,
                               scale: Optional[float] = None, out=None, lse=None,
                               want_lse: bool = False, workspace=None, count=None, idx=None,
-                              want_lists: bool = False, k_new=None, v_new=None):
+                              want_lists: bool = False, k_new=None, v_new=None, head_wb=None):
     """Decode with the keep-set computed in the kernel from (pos, prompt_len,
     mask) -- one launch for build + attention.  q [n_q, hq, hd]; caches as in
     ``kv_cache``; seq/pos/prompt_len [n_q] int32.  With ``want_lists`` (or
     given count/idx) the lists keepset_build would write are written too.
     k_new/v_new [n_q, hkv, hd]: the new token's K/V rows, appended to the
-    cache at pos before attention (one query per request).
+    cache at pos before attention (one query per request).  head_wb
+    [hkv, 2] int32 on the device: a (W, B) per kv head.
     Returns (out, lse or None, count or None, idx or None)."""
     _need_cuda("sparse_decode_attn_masked", q, k_cache, v_cache, seq, pos, prompt_len, block_table,
-               k_new, v_new)
+               k_new, v_new, head_wb)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [n_q, hq, hd] tensor")
     if q.dtype not in _DTYPE or q.dtype != k_cache.dtype:
@@ -200,6 +201,9 @@ def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
         raise ValueError("idx must be a contiguous int32 [n_q, cap] tensor, count int32 [n_q]")
     if (k_new is None) != (v_new is None):
         raise ValueError("k_new and v_new go together")
+    if head_wb is not None and (head_wb.dtype != torch.int32 or not head_wb.is_contiguous() or
+                                tuple(head_wb.shape) != (hkv, 2)):
+        raise ValueError("head_wb must be a contiguous int32 [hkv, 2] tensor")
     for t in (k_new, v_new):
         if t is not None and (t.dtype != q.dtype or not t.is_contiguous() or
                               tuple(t.shape) != (n_q, hkv, hd)):
@@ -210,7 +214,7 @@ def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
     kv = kv_cache(k_cache, v_cache, block_table)
     check(load().da_sparse_decode_attn_masked(m, _ptr(q), _DTYPE[q.dtype], n_q, hq, hkv, hd,
                                               float(scale), kv, _ptr(seq), _ptr(pos),
-                                              _ptr(prompt_len), _ptr(k_new), _ptr(v_new),
+                                              _ptr(prompt_len), _ptr(head_wb), _ptr(k_new), _ptr(v_new),
                                               cap, split, _ptr(count), _ptr(idx),
                                               _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                               _stream(q)),

@@ -68,8 +68,10 @@ struct DecodeArgs {
   float* lse;
   float* ws_o;            // [n_q][hq][max_split][HD]
   float* ws_ml;           // [n_q][hq][max_split][2]
-  int32_t* ws_cnt;        // [n_q] keep-set sizes (mask form, several chunks)
-  const int32_t* mcount;  // the sizes the merge reads: count (lists) or ws_cnt
+  int32_t* ws_cnt;        // [n_q][hkv] keep-set sizes (mask form, several chunks)
+  const int32_t* mcount;  // the sizes the merge reads: count [n_q] (lists) or ws_cnt
+  int mcount_per_head;    // mcount indexed by (query, kv head) instead of query
+  const int32_t* head_wb; // mask form: per-kv-head (W, B) [hkv][2], or null
 };
 
 // Workspace layout: partial outputs, then partial (max, sum) pairs, then
@@ -87,7 +89,7 @@ static WsLayout ws_layout(int64_t n_q, int64_t hq, int64_t hd, int64_t ns) {
   w.o_off = 0;
   w.ml_off = align256(rows * hd * 4);
   w.cnt_off = w.ml_off + align256(rows * 2 * 4);
-  w.bytes = w.cnt_off + align256(n_q * 4);
+  w.bytes = w.cnt_off + align256(n_q * hq * 4);
   return w;
 }
 
@@ -271,6 +273,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const int i = a.pos[qi];
     const int P = a.prompt[qi];
     const int sq_raw = a.seq[qi];
+    // the mask's window and band, or this kv head's own (negative read as 0)
+    const int Wm = a.head_wb ? (a.head_wb[2 * g] > 0 ? a.head_wb[2 * g] : 0) : a.W;
+    const int Bm = a.head_wb ? (a.head_wb[2 * g + 1] > 0 ? a.head_wb[2 * g + 1] : 0) : a.B;
     // KV append: lanes 0 .. LPR-1 carry the new token's K chunk of this kv
     // head, lanes LPR .. 2 LPR-1 its V chunk
     const bool appending = a.k_new != nullptr;
@@ -305,7 +310,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         Pc = L;
       } else {
         Pc = P < L ? P : L;
-        wlo = i - a.W > Pc ? i - a.W : Pc;
+        wlo = i - Wm > Pc ? i - Wm : Pc;
         whi = i;
       }
     }
@@ -322,7 +327,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     int n = Pc;
     for (int base = wlo; base <= whi; base += 256) {
       const int j = base + t;
-      const bool kp = j <= whi && window_keep(a.mode, i - j, a.B, a.G);
+      const bool kp = j <= whi && window_keep(a.mode, i - j, Bm, a.G);
       const uint64_t bal = __ballot(kp);
       if (lane == 0) wcount[wave_id] = __popcll(bal);
       __syncthreads();
@@ -341,7 +346,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       __syncthreads();                                // wcount is reused
     }
     if (lists && s == 0 && t == 0) a.count_out[qi] = n;
-    if (a.ws_cnt && g == 0 && s == 0 && t == 0) a.ws_cnt[qi] = n;
+    if (a.ws_cnt && s == 0 && t == 0) a.ws_cnt[(int64_t)qi * a.hkv + g] = n;
     cnt = n < a.cap ? n : a.cap;
     // KV append, several chunks: the chunk that attends the last entry
     // (position i itself when the list is not truncated) stores the new row
@@ -513,7 +518,7 @@ __global__ void __launch_bounds__(64) merge_kernel(DecodeArgs a) {
   const int row = blockIdx.x;           // query * hq + head
   const int qi = row / a.hq;
   const int lane = threadIdx.x;
-  int cnt = a.mcount[qi];
+  int cnt = a.mcount[a.mcount_per_head ? (int64_t)qi * a.hkv + (row % a.hq) / (a.hq / a.hkv) : qi];
   cnt = cnt < a.cap ? cnt : a.cap;
   if (cnt <= a.split) return;           // written directly by decode_kernel
   const int ns = (cnt + a.split - 1) / a.split;
@@ -729,6 +734,7 @@ extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_
                                             int32_t n_q, int32_t hq, int32_t hkv, int32_t head_dim,
                                             float scale, const da_kv_cache* kv, const int32_t* seq,
                                             const int32_t* pos, const int32_t* prompt_len,
+                                            const int32_t* head_wb,
                                             const void* k_new, const void* v_new,
                                             int32_t cap, int32_t split, int32_t* count, int32_t* idx,
                                             void* out, float* lse, void* workspace, int64_t ws_bytes,
@@ -745,6 +751,8 @@ extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_
     return fail(DA_EINVAL, "count and idx must both be given or both be NULL");
   if ((k_new == nullptr) != (v_new == nullptr))
     return fail(DA_EINVAL, "k_new and v_new must both be given or both be NULL");
+  if (head_wb && count)
+    return fail(DA_EINVAL, "per-head masks give per-head keep-sets: no per-query lists");
   if (((uintptr_t)k_new | (uintptr_t)v_new) % 16) return fail(DA_EINVAL, "k_new and v_new must be 16-byte aligned");
   clear_error();
   if (n_q == 0) return DA_OK;
@@ -759,5 +767,7 @@ extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_
   a.count_out = count;
   a.idx_out = idx;
   a.mcount = a.ws_cnt;                  // written by the decode kernel when there is a merge
+  a.mcount_per_head = 1;
+  a.head_wb = head_wb;
   return launch_decode<true>(a, dtype, head_dim, stream);
 }

@@ -441,6 +441,31 @@ def mask_sweep(b, steps, warmup, w_rows=(1, 2, 3, 6), bands=(0, 1, 2, 4)):
     return rows
 
 
+def per_head_run(b, steps, warmup):
+    """Per-kv-head windows at the benchmark shape: kv heads alternate between
+    a window of one raster row and of three (B unchanged), as a per-head
+    budget would set them.  Returns the step time and kept bytes."""
+    torch, da = b.torch, b.da
+    cfg = b.cfg
+    wb = [[cfg.G * (1 if g % 2 == 0 else 3), cfg.B] for g in range(cfg.hkv)]
+    head_wb = torch.tensor(wb, dtype=torch.int32, device=b.q.device)
+    m = da.mask(cfg.modes[0], cfg.W, cfg.B, cfg.G)
+    maxpos, maxp = int(b.inp.pos.max()), int(b.inp.prompt_len.max())
+    cap = max(da.keep_cap(da.mask(cfg.modes[0], w, bb, cfg.G), maxpos, maxp) for w, bb in wb)
+    out = torch.empty_like(b.q)
+
+    def run(c):
+        da.sparse_decode_attn_masked(m, b.q, b.k, b.v, b.seqs[c], b.pos, b.prompt, cap=cap,
+                                     split=max(cap, 1), block_table=b.bts[c], out=out,
+                                     head_wb=head_wb)
+    us = graph_us(torch, run, b.n_copies, steps, warmup)
+    row = 2 * cfg.hd * (2 if cfg.dtype == "bf16" else 4)
+    kept = sum(da.keep_count(da.mask(cfg.modes[0], w, bb, cfg.G), int(p), int(P))
+               for w, bb in wb for p, P in zip(*b.hosts)) * row
+    return {"head_W": [w for w, _ in wb], "us_per_step": round(us, 2),
+            "kept_MB": round(kept / 1e6, 3), "kept_GBps": round(kept / (us * 1e-6) / 1e9, 1)}
+
+
 def burn_in(bufs, seconds):
     """Streams the given device tensors until `seconds` have passed, so the
     memory and core clocks have left their idle states before anything is
@@ -757,6 +782,10 @@ def main():
     traffic = traffic_from_profile(cfg.name)
 
     sweep = mask_sweep(b, K, W) if not args.no_extra else None
+    per_head = per_head_run(b, K, W) if not args.no_extra else None
+    if per_head:
+        log(f"[bench] per-head windows {per_head['head_W'][:4]}...: {per_head['us_per_step']:.2f} us, "
+            f"{per_head['kept_MB']:.1f} MB kept, {per_head['kept_GBps']:.0f} GB/s")
 
     # keep-set-aware KV residency: the same step through a ring block table
     residency = {}
@@ -869,6 +898,7 @@ def main():
         "extra": extra,
         "kv_residency": residency,
         "mask_sweep": sweep,
+        "per_head_masks": per_head,
         "prefill": prefill,
     }
     print(json.dumps(line), flush=True)

@@ -145,7 +145,8 @@ typedef struct {
 /* [host] Workspace bytes da_sparse_decode_attn and da_sparse_decode_attn_masked
  * need for these sizes (0 when every keep-set fits one chunk, i.e. cap <=
  * split): the per-chunk partial results (max, sum, unnormalised output) that
- * the merge kernel combines, and (mask form) each query's keep-set size. */
+ * the merge kernel combines, and (mask form) the keep-set size of each
+ * (query, kv head). */
 int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t head_dim,
                                   int32_t cap, int32_t split);
 
@@ -202,6 +203,11 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
  *   count, idx  optional outputs (both or neither): the lists exactly as
  *          da_keepset_build writes them (count[q] the true size; idx[q*cap+r]
  *          for r < min(count[q], cap)), for callers that reuse them
+ *   head_wb optional [hkv][2] int32: a window and band (W, B) per kv head,
+ *          replacing m->W, m->B for that head (adaptive / per-head budgets;
+ *          negative values read as 0).  The query heads of a kv head share
+ *          its keep-set, so each kept row is still read once.  Not allowed
+ *          with count/idx (those lists are per query).
  *   k_new, v_new optional inputs (both or neither) [n_q][hkv][head_dim] in
  *          `dtype`, 16-byte aligned: KV append.  The row of each query's own
  *          position pos[q] is written into the cache (kv->k, kv->v, which must
@@ -215,13 +221,15 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
  * written for that query; positions and requests are clamped into the
  * descriptor's extents.
  * Errors: as da_sparse_decode_attn, plus DA_EINVAL for an invalid mask, null
- * pos/prompt_len, only one of count/idx or of k_new/v_new given, or
- * misaligned k_new/v_new; DA_ENOTSUP for causal = 0. */
+ * pos/prompt_len, only one of count/idx or of k_new/v_new given, head_wb
+ * together with count/idx, or misaligned k_new/v_new; DA_ENOTSUP for
+ * causal = 0. */
 int da_sparse_decode_attn_masked(const da_mask* m /* [host] */, const void* q,
                                  da_dtype dtype, int32_t n_q, int32_t hq, int32_t hkv,
                                  int32_t head_dim, float scale,
                                  const da_kv_cache* kv /* [host] */, const int32_t* seq,
                                  const int32_t* pos, const int32_t* prompt_len,
+                                 const int32_t* head_wb,
                                  const void* k_new, const void* v_new,
                                  int32_t cap, int32_t split, int32_t* count, int32_t* idx,
                                  void* out, float* lse, void* workspace, int64_t ws_bytes,

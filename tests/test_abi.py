@@ -105,10 +105,10 @@ def test_argument_errors_are_reported_before_launch():
     assert dec(q=ctypes.c_void_p(8)) == -1   # misaligned q
 
     def dec_m(mk=m, n_q=1, hq=8, hkv=2, hd=128, cap=64, split=64, pos=dummy, count=None, idx=None,
-              k_new=None, v_new=None):
+              k_new=None, v_new=None, head_wb=None):
         return lib.da_sparse_decode_attn_masked(mk, dummy, 1, n_q, hq, hkv, hd, 0.1, kv, dummy, pos,
-                                                dummy, k_new, v_new, cap, split, count, idx, dummy,
-                                                None, None, 0, None)
+                                                dummy, head_wb, k_new, v_new, cap, split, count, idx,
+                                                dummy, None, None, 0, None)
     assert dec_m(mk=bad) == -1
     assert dec_m(mk=nc) == -2 and "causal" in _native.last_error()
     assert dec_m(pos=None) == -1 and "pos" in _native.last_error()
@@ -116,6 +116,7 @@ def test_argument_errors_are_reported_before_launch():
     assert dec_m(hd=96) == -2
     assert dec_m(cap=200, split=64) == -3
     assert dec_m(k_new=dummy) == -1 and "k_new" in _native.last_error()
+    assert dec_m(head_wb=dummy, count=dummy, idx=dummy) == -1 and "per-head" in _native.last_error()
     assert dec_m(k_new=ctypes.c_void_p(8), v_new=dummy) == -1      # misaligned
     assert dec_m(n_q=0, pos=None) == 0     # nothing to do, nothing read
 

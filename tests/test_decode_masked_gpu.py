@@ -248,3 +248,45 @@ def test_random_configurations(seed):
         assert_same(a, b, cap)
         ref_o, ref_l = run_oracle(inp, mode)
         assert_close(b[0], b[1], ref_o, ref_l, cfg.dtype)
+
+
+@pytest.mark.parametrize("split", [32, 4096])
+def test_per_head_masks(split):
+    """A (W, B) per kv head: each group of query heads against the oracle run
+    with its kv head's mask; with the same (W, B) everywhere, bitwise the
+    shared-mask call."""
+    cfg = wl.small_decode("gqa_b64", n_seq=3)
+    inp = wl.decode_inputs(cfg)
+    k, v, bt = caches(inp)
+    rng = np.random.default_rng(7)
+    wb = np.stack([rng.integers(0, 300, cfg.hkv), rng.integers(0, 7, cfg.hkv)], axis=1).astype(np.int32)
+    head_wb = torch.from_numpy(wb).to(dev())
+    args = (inp.q.to(dev()), k, v, inp.seq.to(dev()), inp.pos.to(dev()), inp.prompt_len.to(dev()))
+    maxpos, maxp = int(inp.pos.max()), int(inp.prompt_len.max())
+    grp = cfg.hq // cfg.hkv
+    q = inp.q.double().numpy()
+    K, V = inp.k_logical.double().numpy(), inp.v_logical.double().numpy()
+    for mode in (O.BAND, O.ROWDIAG):
+        m = da.mask(mode, cfg.W, cfg.B, cfg.G)
+        cap = max(da.keep_cap(da.mask(mode, int(w), int(b), cfg.G), maxpos, maxp) for w, b in wb)
+        out, lse, _, _ = da.sparse_decode_attn_masked(m, *args, cap=cap, split=split, block_table=bt,
+                                                      want_lse=True, head_wb=head_wb)
+        torch.cuda.synchronize()
+        ref_o = np.zeros(q.shape)
+        ref_l = np.zeros(q.shape[:2])
+        for g, (w, b) in enumerate(wb):
+            hs = slice(g * grp, (g + 1) * grp)
+            o_g, l_g = O.decode_attention(q[:, hs], K[:, g:g + 1], V[:, g:g + 1], inp.pos.numpy(),
+                                          inp.prompt_len.numpy(), inp.seq.numpy(),
+                                          W=int(w), B=int(b), G=cfg.G, mode=mode)
+            ref_o[:, hs], ref_l[:, hs] = o_g, l_g
+        assert_close(out.cpu(), lse.cpu(), ref_o, ref_l, cfg.dtype)
+    same = torch.tensor([[cfg.W, cfg.B]] * cfg.hkv, dtype=torch.int32, device=dev())
+    m = da.mask(O.ROWDIAG, cfg.W, cfg.B, cfg.G)
+    cap = da.keep_cap(m, maxpos, maxp)
+    o1, l1, _, _ = da.sparse_decode_attn_masked(m, *args, cap=cap, split=split, block_table=bt,
+                                                want_lse=True, head_wb=same)
+    o2, l2, _, _ = da.sparse_decode_attn_masked(m, *args, cap=cap, split=split, block_table=bt,
+                                                want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.cpu(), o2.cpu()) and torch.equal(l1.cpu(), l2.cpu())
