@@ -24,7 +24,7 @@
 // needs agent-scope fences, which write back and invalidate the whole L2 of
 // the XCD on this part: measured far slower than a second launch.)
 //
-// Mask form (MASKED): instead of reading lists, each workgroup builds the
+// Mask form (FORM 1, 2): instead of reading lists, each workgroup builds the
 // entries of its chunk from the query's position, prompt length and the
 // mask with the list builder's rule and order (prompt entries directly, the
 // window by a ballot scan), so keep-set build and attention are one launch;
@@ -171,8 +171,12 @@ __device__ inline int64_t row_offset(const DecodeArgs& a, const int32_t* bt, int
   return (int64_t)sq * a.page_stride + (int64_t)j * a.slot_stride;
 }
 
-template <bool BF16, int HD, int GRP, int NP, bool MASKED>
+// FORM: 0 = listed keys; 1 = keep-set from the mask; 2 = from the mask with
+// a window and band per kv head.
+template <bool BF16, int HD, int GRP, int NP, int FORM>
 __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+  constexpr bool MASKED = FORM >= 1;
+  constexpr bool PERHEAD = FORM == 2;
   using TL = Tile<BF16, HD, NP>;
   constexpr int ES = TL::ES;
   constexpr int EPL = TL::EPL;
@@ -274,8 +278,11 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     const int P = a.prompt[qi];
     const int sq_raw = a.seq[qi];
     // the mask's window and band, or this kv head's own (negative read as 0)
-    const int Wm = a.head_wb ? (a.head_wb[2 * g] > 0 ? a.head_wb[2 * g] : 0) : a.W;
-    const int Bm = a.head_wb ? (a.head_wb[2 * g + 1] > 0 ? a.head_wb[2 * g + 1] : 0) : a.B;
+    int Wm = a.W, Bm = a.B;
+    if constexpr (PERHEAD) {
+      Wm = a.head_wb[2 * g] > 0 ? a.head_wb[2 * g] : 0;
+      Bm = a.head_wb[2 * g + 1] > 0 ? a.head_wb[2 * g + 1] : 0;
+    }
     // KV append: lanes 0 .. LPR-1 carry the new token's K chunk of this kv
     // head, lanes LPR .. 2 LPR-1 its V chunk
     const bool appending = a.k_new != nullptr;
@@ -558,28 +565,28 @@ typedef void (*decode_fn)(DecodeArgs);
 typedef void (*merge_fn)(DecodeArgs);
 
 // Tile depth: NP passes per tile (two tiles in flight per workgroup).
-template <bool BF16, int HD, int GRP, bool MASKED>
+template <bool BF16, int HD, int GRP, int FORM>
 static decode_fn pick_np(int np) {
-  if (np <= 2) return decode_kernel<BF16, HD, GRP, 2, MASKED>;
-  if (np == 3) return decode_kernel<BF16, HD, GRP, 3, MASKED>;
-  return decode_kernel<BF16, HD, GRP, 4, MASKED>;
+  if (np <= 2) return decode_kernel<BF16, HD, GRP, 2, FORM>;
+  if (np == 3) return decode_kernel<BF16, HD, GRP, 3, FORM>;
+  return decode_kernel<BF16, HD, GRP, 4, FORM>;
 }
 
-template <bool BF16, int HD, bool MASKED>
+template <bool BF16, int HD, int FORM>
 static decode_fn pick_grp(int grp, int np) {
   switch (grp) {
-    case 1: return pick_np<BF16, HD, 1, MASKED>(np);
-    case 2: return pick_np<BF16, HD, 2, MASKED>(np);
-    case 4: return pick_np<BF16, HD, 4, MASKED>(np);
-    default: return pick_np<BF16, HD, 8, MASKED>(np);
+    case 1: return pick_np<BF16, HD, 1, FORM>(np);
+    case 2: return pick_np<BF16, HD, 2, FORM>(np);
+    case 4: return pick_np<BF16, HD, 4, FORM>(np);
+    default: return pick_np<BF16, HD, 8, FORM>(np);
   }
 }
 
-template <bool MASKED>
+template <int FORM>
 static decode_fn pick_kernel(da_dtype dtype, int head_dim, int grp, int np) {
   if (dtype == DA_BF16)
-    return head_dim == 64 ? pick_grp<true, 64, MASKED>(grp, np) : pick_grp<true, 128, MASKED>(grp, np);
-  return head_dim == 64 ? pick_grp<false, 64, MASKED>(grp, np) : pick_grp<false, 128, MASKED>(grp, np);
+    return head_dim == 64 ? pick_grp<true, 64, FORM>(grp, np) : pick_grp<true, 128, FORM>(grp, np);
+  return head_dim == 64 ? pick_grp<false, 64, FORM>(grp, np) : pick_grp<false, 128, FORM>(grp, np);
 }
 
 // Row slots past a list's end still issue their (redundant) loads, and on
@@ -681,12 +688,12 @@ static int prepare_decode(DecodeArgs& a, const void* q, da_dtype dtype, int32_t 
 
 // Launches the decode kernel (and, when a list spans several chunks, the
 // merge) for prepared arguments.
-template <bool MASKED>
+template <int FORM>
 static int launch_decode(const DecodeArgs& a, da_dtype dtype, int head_dim, void* stream) {
   const int esz = dtype == DA_BF16 ? 2 : 4;
   const int chunk = a.split < a.cap ? a.split : a.cap;
   const int np = tile_depth(chunk, 256 / (head_dim * esz / 16));
-  const decode_fn dk = pick_kernel<MASKED>(dtype, head_dim, a.hq / a.hkv, np);
+  const decode_fn dk = pick_kernel<FORM>(dtype, head_dim, a.hq / a.hkv, np);
   const merge_fn mk = dtype == DA_BF16 ? (head_dim == 64 ? merge_kernel<true, 64> : merge_kernel<true, 128>)
                                        : (head_dim == 64 ? merge_kernel<false, 64> : merge_kernel<false, 128>);
   const int64_t blocks = int64_t(a.n_q) * a.hkv * a.max_split;
@@ -727,7 +734,7 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
   a.idx = idx;
   a.mcount = count;
   a.ws_cnt = nullptr;                   // the merge reads the lists' counts
-  return launch_decode<false>(a, dtype, head_dim, stream);
+  return launch_decode<0>(a, dtype, head_dim, stream);
 }
 
 extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_dtype dtype,
@@ -769,5 +776,6 @@ extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_
   a.mcount = a.ws_cnt;                  // written by the decode kernel when there is a merge
   a.mcount_per_head = 1;
   a.head_wb = head_wb;
-  return launch_decode<true>(a, dtype, head_dim, stream);
+  return head_wb ? launch_decode<2>(a, dtype, head_dim, stream)
+                 : launch_decode<1>(a, dtype, head_dim, stream);
 }
