@@ -79,13 +79,6 @@ __device__ inline bool range_all_kept(int ilo, int jhi, int P, int mode) {
   return mode == DA_MODE_DENSE || jhi < P;
 }
 
-__device__ inline bool keep_pair(int i, int j, int P, int mode, int W, int B, int G) {
-  if (j > i) return false;
-  if (mode == DA_MODE_DENSE || j < P) return true;
-  const int d = i - j;
-  return d <= W && window_keep(mode, d, B, G);
-}
-
 // s_waitcnt immediate that waits until at most n vector-memory operations
 // of this wave are outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
