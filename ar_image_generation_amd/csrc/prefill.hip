@@ -1,11 +1,13 @@
 // band_prefill_attn: causal, keep-set-masked attention over whole sequences,
 // bf16 in, fp32 accumulation, on the matrix cores (v_mfma_f32_16x16x32_bf16).
 //
-// Workgroup = 8 waves = 256 query rows of one (batch, head); each wave owns
+// Workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
 // two blocks of 16 rows.  The 64-key tiles that hold a kept pair (listed
-// once per query tile by prefill_tiles_kernel) stream K and V into a ring of
-// four LDS stages by direct global->LDS copies; the loop takes them in
-// steps of two tiles, fetching the next pair while it computes.  Scores are
+// once per query tile by prefill_tiles_kernel) stream K and V into a
+// two-stage LDS ring by direct global->LDS copies, the next tile in flight
+// while the current one is computed.  A workgroup takes at most 80 KiB of
+// LDS, so two share a CU: while one waits at its per-tile barrier the
+// other's matrix work keeps the CU busy.  Scores are
 // computed transposed, S^T = K Q^T (A = K from LDS, B = Q^T from
 // registers), so that the MFMA result gives every lane one query row and
 // four keys of each 16-key block.  That lane-per-row layout is kept for the
@@ -48,7 +50,8 @@ struct PrefillArgs {
 
 // Query tile: NWAVE waves x RB_MAX row blocks of 16 rows; key tile: BN keys.
 constexpr int RB_MAX = 2;
-constexpr int NWAVE = 8;
+constexpr int NWAVE = 4;
+static_assert(NWAVE * 8 <= 32, "the LDS list keeps 8 full-block bits per wave in 32 bits");
 constexpr int BM_ROWS = NWAVE * 16 * RB_MAX;
 constexpr int NTHREADS = NWAVE * 64;
 
@@ -104,7 +107,7 @@ __device__ inline uint64_t bit_range(int lo, int hi) {
 // (one 64-bit word per residue mod G) lives in LDS.
 constexpr int GMAX = 1024;
 
-// Longest tile list a query tile may have (LDS copy, 16 bytes an entry):
+// Longest tile list a query tile may have (LDS copy, 8 bytes an entry):
 // sequences of up to 64 * MAX_LIST tokens.
 constexpr int MAX_LIST = 1024;
 
@@ -196,7 +199,7 @@ __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
 
 // ---------------------------------------------------------------- attention
 template <int HD, int MODE>
-__global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2))) prefill_kernel(PrefillArgs a) {
   constexpr int RB = RB_MAX;
   constexpr int NC = HD / 32;          // 32-wide contraction chunks of the head dim
   constexpr int NB = HD / 16;          // 16-wide output blocks of the head dim
@@ -204,7 +207,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   constexpr int RPI = 64 / CPR;        // key rows per 1 KiB wave transfer
   constexpr int TILE = BN * HD;        // elements of one K (or V) tile
   constexpr int DPW = BN * CPR / NTHREADS;  // 1 KiB transfers per wave per tile, K (same for V)
-  constexpr int NS = 4;                // LDS ring stages (see the loop below)
+  constexpr int NS = 2;                // LDS ring stages: current tile, next tile
 
   // ring of NS stages, each a K tile then a V tile, row-major, 16-byte
   // chunk p of row r holding the row's chunk p ^ swz(r) (bank spreading)
@@ -212,9 +215,9 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   // row-diagonal band pattern: bit c of bp[r] says whether a key c places
   // before a query at residue r (mod G) lies within B of a multiple of G
   __shared__ uint64_t bp[MODE == DA_MODE_ROWDIAG ? GMAX : 1];
-  // this query tile's list: (key tile, full-block mask lo, hi, 0); read
+  // this query tile's list: (key tile, full-block bits of waves 0..3); read
   // from LDS so that no list read waits behind the tile DMA in flight
-  __shared__ int4 tl[MAX_LIST];
+  __shared__ int2 tl[MAX_LIST];
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches
@@ -278,12 +281,11 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
   for (int e = t; e < cnt; e += NTHREADS) {
     const int4 e0 = list[2 * e];
     const int4 e1 = list[2 * e + 1];
-    tl[e] = make_int4(clampi(e0.x, 0, jt_max), e1.x, e1.y, 0);
+    tl[e] = make_int2(clampi(e0.x, 0, jt_max), e1.x);
   }
   __syncthreads();
 
   issue(tl[0].x, 0);
-  if (cnt > 1) issue(tl[1].x, 1);
 
   if constexpr (MODE == DA_MODE_ROWDIAG) {
     // band centres of residue r within reach of bits 0..63: r - kG for
@@ -330,9 +332,9 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
 
   // Masks: a 64-bit keep word per row over the keys of the tile whose first
   // key is j0 -- causal bits, prompt bits and the window rule -- applied to
-  // that tile's four 16-key score blocks (half 0 or 1 of a step): each score
-  // the lane holds (key 16kq + 4lg + r) keeps its bit or becomes -inf.
-  auto apply_mask = [&](f32x4 (&sc)[RB][8], int half, int j0) {
+  // that tile's four 16-key score blocks: each score the lane holds
+  // (key 16kq + 4lg + r) keeps its bit or becomes -inf.
+  auto apply_mask = [&](f32x4 (&sc)[RB][4], int j0) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int x = my_i0 + 16 * rb - j0;
@@ -348,18 +350,17 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int32_t m = (int32_t)(wd[kq >> 1] << (31 - (16 * (kq & 1) + r))) >> 31;
-          sc[rb][4 * half + kq][r] =
-              __int_as_float((__float_as_int(sc[rb][4 * half + kq][r]) & m) | (~m & (int32_t)0xff800000));
+          sc[rb][kq][r] = __int_as_float((__float_as_int(sc[rb][kq][r]) & m) | (~m & (int32_t)0xff800000));
         }
     }
   };
   // S^T = K Q^T for the four 16-key blocks of one staged tile (A = K from
-  // LDS, shared by the RB row blocks), into half `half` of a step's scores
-  auto scores_into = [&](const uint16_t* ksm, f32x4 (&sc)[RB][8], int half) {
+  // LDS, shared by the RB row blocks)
+  auto scores_into = [&](const uint16_t* ksm, f32x4 (&sc)[RB][4]) {
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sc[rb][4 * half + kq] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < RB; ++rb) sc[rb][kq] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int row = 16 * kq + lr;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -367,45 +368,32 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ksm + row * HD + pos * 8);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          sc[rb][4 * half + kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][4 * half + kq], 0, 0, 0);
+          sc[rb][kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][kq], 0, 0, 0);
       }
     }
   };
 
-  // Steps of two listed tiles (128 keys): one wait and one barrier per step,
-  // one max / rescale, P.V over four 32-key chunks.  Tile t lives in stage
-  // t % NS.  At the top of step idx tiles idx and idx+1 have landed and all
-  // waves are done with step idx-2, whose stages then receive tiles idx+2
-  // and idx+3 -- fetched while this step computes.
-  __syncthreads();                     // tiles 0 and 1 landed, band pattern written
-  for (int idx = 0; idx < cnt; idx += 2) {
+  // One listed tile a step, tile t in stage t % NS.  At the top of step idx
+  // tile idx has landed and every wave is done with step idx-1, whose stage
+  // then receives tile idx+1 -- fetched while this step computes.  The
+  // DMA is invisible to the compiler's waits: each wave waits for its own
+  // part (vmcnt), then the barrier covers every wave's part.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();                     // tile 0 landed, band pattern written
+  for (int idx = 0; idx < cnt; ++idx) {
     if (idx > 0) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // tiles idx, idx+1 (this wave's part)
-      __builtin_amdgcn_s_barrier();               // everyone's part; step idx-2 done
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // tile idx (this wave's part)
+      __builtin_amdgcn_s_barrier();               // everyone's part; step idx-1 done
       __asm__ volatile("" ::: "memory");
     }
-    if (idx + 2 < cnt) issue(tl[idx + 2].x, (idx + 2) % NS);
-    if (idx + 3 < cnt) issue(tl[idx + 3].x, (idx + 3) % NS);
-    const bool two = idx + 1 < cnt;
-    const int4 e0 = tl[idx];
-    const int4 e1 = tl[two ? idx + 1 : idx];
-    const unsigned full0 = (unsigned)((((uint64_t)(uint32_t)e0.y | ((uint64_t)(uint32_t)e0.z << 32)) >> (wave * 8)) & 0xffu);
-    const unsigned full1 = (unsigned)((((uint64_t)(uint32_t)e1.y | ((uint64_t)(uint32_t)e1.z << 32)) >> (wave * 8)) & 0xffu);
+    if (idx + 1 < cnt) issue(tl[idx + 1].x, (idx + 1) % NS);
+    const int2 e0 = tl[idx];
+    const unsigned full0 = ((uint32_t)e0.y >> (wave * 8)) & 0xffu;
     const uint16_t* st0 = ring + (idx % NS) * 2 * TILE;
-    const uint16_t* st1 = ring + ((idx + 1) % NS) * 2 * TILE;
 
-    f32x4 sc[RB][8];
-    scores_into(st0, sc, 0);
-    if (two) {
-      scores_into(st1, sc, 1);
-    } else {                           // odd count: the second half is empty
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int kq = 4; kq < 8; ++kq) sc[rb][kq] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    }
-    if (full0 != 0xffu) apply_mask(sc, 0, e0.x * BN);
-    if (two && full1 != 0xffu) apply_mask(sc, 1, e1.x * BN);
+    f32x4 sc[RB][4];
+    scores_into(st0, sc);
+    if (full0 != 0xffu) apply_mask(sc, e0.x * BN);
 
     float mts[RB];
     bool grow = false;
@@ -413,7 +401,7 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
     for (int rb = 0; rb < RB; ++rb) {
       float mt = -INFINITY;
 #pragma unroll
-      for (int kq = 0; kq < 8; ++kq)
+      for (int kq = 0; kq < 4; ++kq)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[rb][kq][r]);
       mts[rb] = max_over_row_groups(mt) * a.qscale;
@@ -432,12 +420,12 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
         mq[rb] = mn;
       }
     }
-    bf16x8 pb[RB][4];
+    bf16x8 pb[RB][2];                // P^T of the tile's two 32-key chunks
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float mref = mq[rb] == -INFINITY ? 0.f : mq[rb];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sc[rb][2 * cc + e / 4][e % 4], a.qscale, -mref));
@@ -445,29 +433,27 @@ __global__ void __launch_bounds__(NTHREADS) prefill_kernel(PrefillArgs a) {
           pb[rb][cc][e] = (__bf16)p;
         }
     }
-    auto pv = [&](const uint16_t* vsm, int cbase) {
+    // O^T += V^T P^T over the tile's two 32-key chunks
+    const uint16_t* vsm = st0 + TILE;
 #pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
+    for (int ch = 0; ch < 2; ++ch) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          typedef short v4i16 __attribute__((ext_vector_type(4)));
-          const int chunk = 2 * nb + (vt_sub >> 1);
-          const int r_lo = 32 * ch + vt_row, r_hi = r_lo + 16;
-          const uint16_t* plo = vsm + r_lo * HD + ((chunk ^ swz<CPR>(r_lo)) * 8) + (vt_sub & 1) * 4;
-          const uint16_t* phi = vsm + r_hi * HD + ((chunk ^ swz<CPR>(r_hi)) * 8) + (vt_sub & 1) * 4;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
-          typedef short v8i16 __attribute__((ext_vector_type(8)));
-          const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+      for (int nb = 0; nb < NB; ++nb) {
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        const int chunk = 2 * nb + (vt_sub >> 1);
+        const int r_lo = 32 * ch + vt_row, r_hi = r_lo + 16;
+        const uint16_t* plo = vsm + r_lo * HD + ((chunk ^ swz<CPR>(r_lo)) * 8) + (vt_sub & 1) * 4;
+        const uint16_t* phi = vsm + r_hi * HD + ((chunk ^ swz<CPR>(r_hi)) * 8) + (vt_sub & 1) * 4;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
+        typedef short v8i16 __attribute__((ext_vector_type(8)));
+        const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][cbase + ch], o[rb][nb], 0, 0, 0);
-        }
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][ch], o[rb][nb], 0, 0, 0);
       }
-    };
-    pv(st0 + TILE, 0);
-    if (two) pv(st1 + TILE, 2);
+    }
   }
 
   // ---- normalise and store: lane holds row wi0+16rb+lr, dims 16nb + 4lg + r

@@ -275,17 +275,17 @@ int64_t da_prefill_tiles_bytes(int32_t batch, int32_t n);
 
 /* prefill_tiles_build -- the tile lists of the keep-set for prefill.
  *
- * Queries are cut into tiles of 256 rows (8 waves x 2 blocks of 16) and keys
+ * Queries are cut into tiles of 128 rows (4 waves x 2 blocks of 16) and keys
  * into tiles of 64 (4 blocks of 16).  For each batch b and query tile qt
  * this writes, in key order, the key tiles that hold at least one kept
  * (row, key) pair of the causal keep rule (prompt_len[b] prompt tokens), and
  * for each two 64-bit masks over (wave w, row block rb, key block kq), bit
  * w*8 + rb*4 + kq: the block holds a kept pair / every pair of the block is
- * kept.  Layout of `tiles` (16-byte aligned, da_prefill_tiles_bytes long):
+ * kept (bits 32..63, waves 4..7, are zero with 4 waves a tile).  Layout of `tiles` (16-byte aligned, da_prefill_tiles_bytes long):
  *   int32 count[batch][n_qt], padded to 16 bytes, then
  *   int32 entry[batch][n_qt][max_tiles][8] = {key tile, need lo, need hi, 0,
  *                                             full lo, full hi, 0, 0}
- * with n_qt = ceil(n / 256), max_tiles = ceil(n / 64).  The lists depend only
+ * with n_qt = ceil(n / 128), max_tiles = ceil(n / 64).  The lists depend only
  * on the mask, n and prompt_len: build them once and reuse them for every
  * head and layer.
  * Errors: DA_EINVAL (mask, sizes, null pointers, alignment), DA_ENOTSUP
