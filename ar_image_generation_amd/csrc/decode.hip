@@ -162,6 +162,14 @@ __device__ inline float chunk_dot(const u32x4 q, const u32x4 k, const float* qf)
   }
 }
 
+// Workgroup barrier that orders LDS only: global loads in flight stay in
+// flight (a plain __syncthreads also waits for every outstanding load).
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Element offset of position j of request sq (contiguous or paged cache).
 __device__ inline int64_t row_offset(const DecodeArgs& a, const int32_t* bt, int sq, int j) {
   j = clampi(j, 0, a.max_len - 1);
@@ -214,6 +222,26 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   int cnt, nrows, sq;
   const int32_t* bt;
   int64_t off0;
+  const char* kb = reinterpret_cast<const char*>(a.k) + ((int64_t)g * a.head_stride + c * EPL) * ES;
+  const char* vb = reinterpret_cast<const char*>(a.v) + ((int64_t)g * a.head_stride + c * EPL) * ES;
+  TL b0, b1;
+  // mask form: chunk rows below pe are prompt entries loaded before the
+  // scan (pe = 0: none); sub_row is the chunk row of the appended token, or -1
+  int pe = 0, sub_row = -1;
+  __shared__ u32x4 newrow[2 * LPR];       // mask form, KV append: the new K, V rows
+  // prompt rows of tile tt, issued before the keep-set scan so that their
+  // loads overlap it (the other lanes' slots are filled after the scan)
+  auto load_prompt = [&](TL& b, int tt) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int r = tt * ROWS + p * RPP + rsub;
+      if (r < pe) {
+        const int64_t o = row_offset(a, bt, sq, r0 + r);
+        b.k[p] = *reinterpret_cast<const u32x4*>(kb + o * ES);
+        b.v[p] = *reinterpret_cast<const u32x4*>(vb + o * ES);
+      }
+    }
+  };
   if constexpr (!MASKED) {
     const int32_t* myidx = a.idx + (int64_t)qi * a.cap + r0;
     int jj[IPT];
@@ -269,10 +297,18 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   } else {
     // ---- keep-set in the kernel: the same rule and order as the list
     // builder.  Entries 0 .. Pc-1 are the prompt (or, DENSE, every key up to
-    // the query); the window [wlo, whi] follows, scanned 256 positions a
-    // round with a ballot per wave and a prefix over the four waves.  Every
-    // entry of this chunk gets its row offset in LDS; with list outputs,
-    // the kv-head-0 workgroups also write the entries of their chunk.
+    // the query), offsets known without the scan.  The window [wlo, whi]
+    // follows, scanned 256 positions a round with a ballot per wave and a
+    // prefix over the four waves.  Every entry of this chunk not loaded yet
+    // gets its row offset in LDS; with list outputs, the kv-head-0
+    // workgroups also write the entries of their chunk.
+    //
+    // A short chunk (at most three tiles, so every tile is in flight at
+    // once) of a contiguous cache loads the prompt rows of its first two
+    // tiles before the scan: their addresses need no memory read, and the
+    // scan's LDS-only barriers leave the loads in flight.  A paged cache
+    // would need block-table reads after them, and every such read waits
+    // for all earlier loads; long chunks stream in the two-buffer loop.
     __shared__ int wcount[4];
     const int i = a.pos[qi];
     const int P = a.prompt[qi];
@@ -299,7 +335,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
               : (int64_t)sq * a.page_stride;
     const bool bad = i < 0 || P < 0;
     // KV append: lanes 0 .. 2 LPR-1 store the new K / V row at position i
-    // (positions outside the cache are not written)
+    // (positions outside the cache are not written).  This workgroup's own
+    // use of the row reads the LDS copy, so no load has to wait for the store.
+    const bool stores = appending && !bad && i < a.max_len;
     auto store_new_row = [&]() {
       if (t < 2 * LPR) {
         const int64_t o = row_offset(a, bt, sq, i);
@@ -307,9 +345,8 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         *reinterpret_cast<u32x4*>(base + ((int64_t)g * a.head_stride + c * EPL + o) * ES) = nkv;
       }
     };
-    // one chunk per query: this workgroup is the only reader of the row, so
-    // it stores now and the store completes under the keep-set scan
-    if (appending && a.max_split == 1 && !bad && i < a.max_len) store_new_row();
+    if (stores && a.max_split == 1) store_new_row();
+    if (appending && t < 2 * LPR) newrow[t] = nkv;
     const int L = i + 1;
     int Pc = 0, wlo = 1, whi = 0;
     if (!bad) {
@@ -322,11 +359,17 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       }
     }
     const int lim_e = r0 + lim;                       // entries of this chunk: [r0, lim_e)
+    const int pc_e = clampi(Pc - r0, 0, lim);        // prompt entries of this chunk
+    if (!bt && lim <= 3 * ROWS) {
+      pe = pc_e;
+      load_prompt(b0, 0);
+      load_prompt(b1, 1);
+    }
     const bool lists = a.count_out != nullptr && g == 0;
     int32_t* my_out = lists ? a.idx_out + (int64_t)qi * a.cap : nullptr;
-    for (int r = r0 + t; r < (Pc < lim_e ? Pc : lim_e); r += 256) {
-      rowoff[r - r0] = row_offset(a, bt, sq, r);
-      if (lists) my_out[r] = r;
+    for (int r = t; r < pc_e; r += 256) {
+      if (r >= pe) rowoff[r] = row_offset(a, bt, sq, r0 + r);
+      if (lists) my_out[r0 + r] = r0 + r;
     }
     const int wave_id = t >> 6;
     const int lane = t & 63;
@@ -337,7 +380,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       const bool kp = j <= whi && window_keep(a.mode, i - j, Bm, a.G);
       const uint64_t bal = __ballot(kp);
       if (lane == 0) wcount[wave_id] = __popcll(bal);
-      __syncthreads();
+      lds_barrier();
       int before = 0, total = 0;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -350,19 +393,22 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
         if (lists) my_out[r] = j;
       }
       n += total;
-      __syncthreads();                                // wcount is reused
+      lds_barrier();                                  // wcount is reused
     }
     if (lists && s == 0 && t == 0) a.count_out[qi] = n;
     if (a.ws_cnt && s == 0 && t == 0) a.ws_cnt[(int64_t)qi * a.hkv + g] = n;
     cnt = n < a.cap ? n : a.cap;
     // KV append, several chunks: the chunk that attends the last entry
     // (position i itself when the list is not truncated) stores the new row
-    // before the barrier below, whose release fence makes it visible to this
-    // workgroup's tile loads.
-    if (appending && a.max_split > 1 && !bad && i < a.max_len && cnt > 0 && (cnt - 1) / a.split == s)
-      store_new_row();
-    __syncthreads();                                  // row offsets (and an appended row) written
-    if (r0 >= cnt) return;
+    if (stores && a.max_split > 1 && cnt > 0 && (cnt - 1) / a.split == s) store_new_row();
+    // the new row is entry n - 1 of the keep-set (position i is always kept);
+    // it is attended unless the list was cut at cap
+    if (stores && n <= a.cap && n - 1 >= r0 && n - 1 < lim_e) sub_row = n - 1 - r0;
+    lds_barrier();                                    // row offsets, new row copy
+    if (r0 >= cnt) {
+      __builtin_amdgcn_s_waitcnt(0);                  // the prompt loads above are dropped
+      return;
+    }
     nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
   }
 
@@ -375,8 +421,6 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const float sscale = BF16 ? a.qscale : 1.f;
 
   // ---- stage 2: tiles of ROWS rows, two in flight; per-thread online softmax
-  const char* kb = reinterpret_cast<const char*>(a.k) + ((int64_t)g * a.head_stride + c * EPL) * ES;
-  const char* vb = reinterpret_cast<const char*>(a.v) + ((int64_t)g * a.head_stride + c * EPL) * ES;
   float m[GRP], l[GRP], acc[GRP][EPL];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
@@ -388,13 +432,29 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int nt = (nrows + ROWS - 1) / ROWS;
 
   auto process = [&](const TL& buf, int tt) {
+    u32x4 kx[NP], vx4[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      kx[p] = buf.k[p];
+      vx4[p] = buf.v[p];
+    }
+    if constexpr (MASKED) {
+      if (sub_row >= 0) {                     // the appended row: its LDS copy
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          if (tt * ROWS + p * RPP + rsub == sub_row) {
+            kx[p] = newrow[c];
+            vx4[p] = newrow[LPR + c];
+          }
+      }
+    }
     float sc[NP][GRP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const bool valid = tt * ROWS + p * RPP + rsub < nrows;
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
-        const float d = group_sum<LPR>(chunk_dot<BF16>(qw[h], buf.k[p], qf[h])) * sscale;
+        const float d = group_sum<LPR>(chunk_dot<BF16>(qw[h], kx[p], qf[h])) * sscale;
         sc[p][h] = valid ? d : -INFINITY;
       }
     }
@@ -415,7 +475,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       float vx[EPL];
-      unpack<EPL>(buf.v[p], vx);
+      unpack<EPL>(vx4[p], vx);
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
         const float w = exp2f(sc[p][h] - mref[h]);
@@ -426,8 +486,37 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     }
   };
 
-  TL b0, b1;
-  if (nt <= 3) {
+  if (MASKED && pe > 0) {
+    // prompt rows of tiles 0 and 1 are in flight: the rest of those two
+    // tiles (window rows from LDS, slots past the chunk position 0's row),
+    // then tile 2 (prompt rows direct); nt <= 3 here
+    auto load_rest = [&](TL& b, int tt) {
+      int64_t o[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int r = tt * ROWS + p * RPP + rsub;
+        o[p] = rowoff[r < nrows ? r : nrows - 1];
+        o[p] = r < nrows ? o[p] : off0;
+        if (tt >= 2 && r < pe) o[p] = row_offset(a, bt, sq, r0 + r);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int r = tt * ROWS + p * RPP + rsub;
+        if (tt >= 2 || r >= pe) {
+          b.k[p] = *reinterpret_cast<const u32x4*>(kb + o[p] * ES);
+          b.v[p] = *reinterpret_cast<const u32x4*>(vb + o[p] * ES);
+        }
+      }
+    };
+    TL b2;
+    load_rest(b0, 0);
+    load_rest(b1, 1);
+    load_rest(b2, 2);
+    process(b0, 0);
+    if (nt > 1) process(b1, 1);
+    if (nt > 2) process(b2, 2);
+  } else if (nt <= 3) {
     // short chunk: every tile in flight at once, none loaded past the end
     // (the two-buffer loop below always issues one tile of lookahead)
     TL b2;

@@ -211,8 +211,8 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
  *   k_new, v_new optional inputs (both or neither) [n_q][hkv][head_dim] in
  *          `dtype`, 16-byte aligned: KV append.  The row of each query's own
  *          position pos[q] is written into the cache (kv->k, kv->v, which must
- *          then be writable) before it is read, so the step attends to the new
- *          token's key and value.  Precondition: no query of the call reads a
+ *          then be writable), and the step attends to these new key and value
+ *          rows at that position (not to what the cache held).  Precondition: no query of the call reads a
  *          row another query of the call appends (e.g. one query per request);
  *          positions outside [0, kv->max_len) are not written.
  *   other arguments as for da_sparse_decode_attn (cap bounds the entries a
