@@ -115,10 +115,13 @@ constexpr int MAX_LIST = 1024;
 // at lds + 16 l).  Issued as inline assembly so that the compiler does not
 // treat it as a pending LDS write that every later LDS read must wait for:
 // the ring's own waits (vmcnt + barrier) order the stages.
-__device__ inline void dma16(const void* src, const void* lds) {
+//
+// The address is a uniform 64-bit base (SGPRs) plus this lane's 32-bit byte
+// offset, so a tile's copies need no per-lane address arithmetic.
+__device__ inline void dma16(const void* sbase, uint32_t voff, const void* lds) {
   const uint32_t dst = __builtin_amdgcn_readfirstlane(
       (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
-  __asm__ volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(dst) : "memory");
+  __asm__ volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(dst) : "memory");
 }
 
 // LDS position of 16-byte chunk p of key row r is p ^ swz(r).  With 16
@@ -247,34 +250,44 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   const uint16_t* vb = a.v + b * a.sv[0] + hk * a.sv[1];
 
   // DMA of key tile jt into ring stage st: this wave's DPW transfers of K
-  // and of V; lane l of transfer u fills LDS chunk l of its 1 KiB block
-  // this lane's rows of a tile and their element offsets (fixed per lane);
-  // a tile adds its first key's offset, rows past the end read the last row
-  int dma_row[DPW];
-  int64_t dma_k[DPW], dma_v[DPW], last_k[DPW], last_v[DPW];
+  // and of V; lane l of transfer u fills LDS chunk l of its 1 KiB block.
+  // This lane's row of each transfer and its byte offsets from the tile's
+  // first row (fixed per lane; under 4 GiB, checked on the host); in the
+  // last tile, rows past the end read the last row instead
+  int dma_row[DPW], dma_c8[DPW];
+  uint32_t dko[DPW], dvo[DPW];
 #pragma unroll
   for (int u = 0; u < DPW; ++u) {
     const int blk = wave * DPW + u;                   // 1 KiB block of the tile
     const int row = blk * RPI + lane / CPR;
     const int chunk = (lane % CPR) ^ swz<CPR>(row);
     dma_row[u] = row;
-    dma_k[u] = (int64_t)row * a.sk[2] + chunk * 8;
-    dma_v[u] = (int64_t)row * a.sv[2] + chunk * 8;
-    last_k[u] = (int64_t)(n - 1) * a.sk[2] + chunk * 8;
-    last_v[u] = (int64_t)(n - 1) * a.sv[2] + chunk * 8;
+    dma_c8[u] = chunk * 8;
+    dko[u] = (uint32_t)(((int64_t)row * a.sk[2] + chunk * 8) * 2);
+    dvo[u] = (uint32_t)(((int64_t)row * a.sv[2] + chunk * 8) * 2);
   }
   auto issue = [&](int jt, int st) {
-    jt = clampi(jt, 0, jt_max);
+    jt = __builtin_amdgcn_readfirstlane(clampi(jt, 0, jt_max));
     uint16_t* kd = ring + st * 2 * TILE;
     uint16_t* vd = kd + TILE;
     const int j0 = jt * BN;
-    const int64_t bk = (int64_t)j0 * a.sk[2], bv = (int64_t)j0 * a.sv[2];
+    const uint16_t* ks = kb + (int64_t)j0 * a.sk[2];
+    const uint16_t* vs = vb + (int64_t)j0 * a.sv[2];
+    if (j0 + BN <= n) {
 #pragma unroll
-    for (int u = 0; u < DPW; ++u) {
-      const int blk = wave * DPW + u;
-      const bool in = j0 + dma_row[u] < n;
-      dma16(kb + (in ? bk + dma_k[u] : last_k[u]), kd + blk * 512);
-      dma16(vb + (in ? bv + dma_v[u] : last_v[u]), vd + blk * 512);
+      for (int u = 0; u < DPW; ++u) {
+        const int blk = wave * DPW + u;
+        dma16(ks, dko[u], kd + blk * 512);
+        dma16(vs, dvo[u], vd + blk * 512);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < DPW; ++u) {
+        const int blk = wave * DPW + u;
+        const int r = j0 + dma_row[u] < n ? dma_row[u] : n - 1 - j0;
+        dma16(ks, (uint32_t)(((int64_t)r * a.sk[2] + dma_c8[u]) * 2), kd + blk * 512);
+        dma16(vs, (uint32_t)(((int64_t)r * a.sv[2] + dma_c8[u]) * 2), vd + blk * 512);
+      }
     }
   };
 
@@ -335,14 +348,23 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   // that tile's four 16-key score blocks: each score the lane holds
   // (key 16kq + 4lg + r) keeps its bit or becomes -inf.
   auto apply_mask = [&](f32x4 (&sc)[RB][4], int j0) {
+    // a tile wholly past the prompt, below every row's diagonal and inside
+    // every row's window needs only the band pattern (uniform per wave)
+    const bool inner = MODE == DA_MODE_ROWDIAG && j0 >= P && wi0 - j0 >= BN - 1 &&
+                       wi0 + 16 * RB - 1 - j0 <= W;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int x = my_i0 + 16 * rb - j0;
-      uint64_t win;
-      if constexpr (MODE == DA_MODE_ROWDIAG) win = bp[mod_g(x, G, a.inv_g)] & bit_range(x - W, x);
-      else if constexpr (MODE == DA_MODE_BAND) win = bit_range(x - (Bw < W ? Bw : W), x);
-      else win = ~uint64_t(0);
-      const uint64_t keep = (win | bit_range(0, P - j0 - 1)) & bit_range(0, x);
+      uint64_t keep;
+      if (inner) {
+        keep = bp[mod_g(x, G, a.inv_g)];
+      } else {
+        uint64_t win;
+        if constexpr (MODE == DA_MODE_ROWDIAG) win = bp[mod_g(x, G, a.inv_g)] & bit_range(x - W, x);
+        else if constexpr (MODE == DA_MODE_BAND) win = bit_range(x - (Bw < W ? Bw : W), x);
+        else win = ~uint64_t(0);
+        keep = (win | bit_range(0, P - j0 - 1)) & bit_range(0, x);
+      }
       const uint64_t sh = keep >> (4 * lg);
       const uint32_t wd[2] = {(uint32_t)sh, (uint32_t)(sh >> 32)};
 #pragma unroll
@@ -550,6 +572,11 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
     return fail(DA_EINVAL, "q, k, v, out, prompt_len and tiles must be non-NULL");
   for (int i = 0; i < 12; ++i)
     if (strides[i] < 0 || (strides[i] * 2) % 16) return fail(DA_EINVAL, "stride %d must be a non-negative multiple of 8 elements", i);
+  // a key tile's rows are addressed by 32-bit byte offsets from its first row
+  if (((int64_t)(BN - 1) * strides[5] + head_dim) * 2 > UINT32_MAX ||
+      ((int64_t)(BN - 1) * strides[8] + head_dim) * 2 > UINT32_MAX)
+    return fail(DA_ENOTSUP, "key/value position stride too large (%lld, %lld elements)",
+                (long long)strides[5], (long long)strides[8]);
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)tiles) % 16)
     return fail(DA_EINVAL, "q, k, v, out and tiles must be 16-byte aligned");
   clear_error();

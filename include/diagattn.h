@@ -320,10 +320,12 @@ int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t
  * and counts are clamped into range, so an inconsistent list gives wrong
  * numbers, never an out-of-bounds access.
  * Limits (LDS copies of the tile list and of the row-diagonal band pattern):
- * n <= 65536 tokens; in ROWDIAG mode G <= 1024.
+ * n <= 65536 tokens; in ROWDIAG mode G <= 1024; the k and v position strides
+ * such that 63 positions plus one row span under 4 GiB (32-bit offsets
+ * within a 64-key tile).
  * Errors: DA_EINVAL (mask, null pointers, sizes, strides, alignment),
  * DA_ENOTSUP (causal = 0, dtype other than bf16, head_dim not 64/128,
- * n > 65536, ROWDIAG with G > 1024). */
+ * n > 65536, ROWDIAG with G > 1024, k/v position stride too large). */
 int da_band_prefill_attn(const da_mask* m /* [host] */, da_dtype dtype, int32_t batch,
                          int32_t heads, int32_t kv_heads, int32_t n, int32_t head_dim,
                          const void* q, const void* k, const void* v, void* out,

@@ -137,6 +137,11 @@ def test_prefill_limits_are_reported_before_launch():
     assert pf(rd, dtype=0) == -2
     assert pf(da.mask(O.ROWDIAG, 64, 1, 32, causal=False)) == -2
     assert pf(rd, n=0) == 0
+    big = (ctypes.c_int64 * 12)(*([128 * 1024, 128 * 1024, 128] * 4))
+    big[5] = 34088000                  # k position stride: a 64-row tile spans > 4 GiB
+    assert lib.da_band_prefill_attn(rd, 1, 1, 2, 2, 1024, 128, dummy, dummy, dummy, dummy, big,
+                                    dummy, dummy, 0.1, None, None) == -2
+    assert "stride too large" in _native.last_error()
 
 
 def test_decode_workspace_size():
