@@ -26,6 +26,8 @@
 // every tile re-reads in that XCD's L2.
 #include "common.h"
 
+#include <type_traits>
+
 namespace da {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -402,16 +404,20 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   // part (vmcnt), then the barrier covers every wave's part.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();                     // tile 0 landed, band pattern written
-  for (int idx = 0; idx < cnt; ++idx) {
+  // the step body takes its ring stage as a constant (the loop runs two
+  // steps an iteration), so every LDS address is a fixed per-lane base
+  // plus an immediate offset
+  auto step = [&](int idx, auto stage) {
+    constexpr int ST = decltype(stage)::value;
     if (idx > 0) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // tile idx (this wave's part)
       __builtin_amdgcn_s_barrier();               // everyone's part; step idx-1 done
       __asm__ volatile("" ::: "memory");
     }
-    if (idx + 1 < cnt) issue(tl[idx + 1].x, (idx + 1) % NS);
+    if (idx + 1 < cnt) issue(tl[idx + 1].x, (ST + 1) % NS);
     const int2 e0 = tl[idx];
     const unsigned full0 = ((uint32_t)e0.y >> (wave * 8)) & 0xffu;
-    const uint16_t* st0 = ring + (idx % NS) * 2 * TILE;
+    const uint16_t* st0 = ring + ST * 2 * TILE;
 
     f32x4 sc[RB][4];
     scores_into(st0, sc);
@@ -476,6 +482,11 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
           o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][ch], o[rb][nb], 0, 0, 0);
       }
     }
+  };
+  static_assert(NS == 2, "two steps an iteration, one per stage");
+  for (int idx = 0; idx < cnt; idx += 2) {
+    step(idx, std::integral_constant<int, 0>{});
+    if (idx + 1 < cnt) step(idx + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and store: lane holds row wi0+16rb+lr, dims 16nb + 4lg + r
