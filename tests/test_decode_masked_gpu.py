@@ -194,6 +194,49 @@ def test_kv_append(name, n_seq, split):
         assert torch.equal(k_miss, k_full) and torch.equal(v_miss, v_full), mode
 
 
+@pytest.mark.parametrize("split", [37, 4096])
+@pytest.mark.parametrize("mode", [O.ROWDIAG, O.BAND, O.DENSE])
+def test_kv_append_query_inside_its_prompt(mode, split):
+    """KV append with some queries inside their prompt (pos < prompt_len):
+    the query's own row is then a prompt entry, which a short chunk of a
+    contiguous cache loads before the keep-set scan, so what that load
+    returns must give way to the appended row.  Equal, bit for bit, to the
+    plain step on the complete cache (one query per request)."""
+    cfg = wl.small_decode("llamagen_b16", n_seq=6)
+    inp = wl.decode_inputs(cfg)
+    n_q = inp.n_q
+    g = torch.Generator().manual_seed(5)
+    pos = torch.randint(0, 90, (n_q,), generator=g, dtype=torch.int32)
+    r = torch.arange(n_q, dtype=torch.int32)
+    prompt = torch.where(r % 2 == 0, pos + 1 + r % 5, pos // 2).to(torch.int32)
+    assert bool((prompt > pos).any()) and bool((prompt <= pos).any())
+    k_full, v_full, _ = caches(inp, paged=False)
+    s_idx, p_idx = inp.seq.long(), pos.long()
+    k_new = inp.k_logical[s_idx, :, p_idx].contiguous().to(dev())
+    v_new = inp.v_logical[s_idx, :, p_idx].contiguous().to(dev())
+    rows = (s_idx.to(dev()), slice(None), p_idx.to(dev()))
+    q, seq = inp.q.to(dev()), inp.seq.to(dev())
+    pos_d, prompt_d = pos.to(dev()), prompt.to(dev())
+    m = da.mask(mode, cfg.W, cfg.B, cfg.G)
+    cap = da.keep_cap(m, int(pos.max()), int(prompt.max()))
+    k_miss, v_miss = k_full.clone(), v_full.clone()
+    k_miss[rows] = 0
+    v_miss[rows] = 0
+    ref, ref_lse, _, _ = da.sparse_decode_attn_masked(m, q, k_full, v_full, seq, pos_d, prompt_d,
+                                                      cap=cap, split=split, want_lse=True)
+    got, got_lse, _, _ = da.sparse_decode_attn_masked(m, q, k_miss, v_miss, seq, pos_d, prompt_d,
+                                                      cap=cap, split=split, want_lse=True,
+                                                      k_new=k_new, v_new=v_new)
+    torch.cuda.synchronize()
+    assert torch.equal(got.cpu(), ref.cpu())
+    assert torch.equal(got_lse.cpu(), ref_lse.cpu())
+    assert torch.equal(k_miss, k_full) and torch.equal(v_miss, v_full)
+    ref_o, ref_l = O.decode_attention(
+        inp.q.double().numpy(), inp.k_logical.double().numpy(), inp.v_logical.double().numpy(),
+        pos.numpy(), prompt.numpy(), inp.seq.numpy(), W=cfg.W, B=cfg.B, G=cfg.G, mode=mode)
+    assert_close(got.cpu(), got_lse.cpu(), ref_o, ref_l, cfg.dtype)
+
+
 def test_mass_share_from_lse_matches_direct_softmax():
     """exp(lse_sparse - lse_dense) is the share of the dense softmax mass on
     the keep-set; compared with that share summed directly in fp64 from the
