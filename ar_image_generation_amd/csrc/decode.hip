@@ -36,6 +36,8 @@
 // kernel read outside the cache.
 #include "common.h"
 
+#include <mutex>
+
 namespace da {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -678,22 +680,63 @@ static decode_fn pick_kernel(da_dtype dtype, int head_dim, int grp, int np) {
   return head_dim == 64 ? pick_grp<false, 64, FORM>(grp, np) : pick_grp<false, 128, FORM>(grp, np);
 }
 
-// Row slots past a list's end still issue their (redundant) loads, and on
-// this part the per-CU load path is what such slots cost: the tile depth is
-// the one of 2, 3 or 4 passes that leaves the fewest empty slots for a chunk
-// of `chunk` rows, ties going to the deeper tile.
-static int tile_depth(int chunk, int rows_per_pass) {
-  int best = 4;
-  int64_t best_slots = INT64_MAX;
-  for (int np = 4; np >= 2; --np) {
-    const int64_t tile = (int64_t)np * rows_per_pass;
-    const int64_t slots = (chunk + tile - 1) / tile * tile;
-    if (slots < best_slots) {
-      best_slots = slots;
-      best = np;
-    }
+// Workgroups of `k` (256 threads, `lds` bytes of dynamic LDS) the current
+// device holds at once, 0 if unknown.  Cached: the answer depends only on the
+// kernel, the LDS size and the device.
+static int64_t resident_blocks(decode_fn k, size_t lds) {
+  struct Entry { decode_fn k; size_t lds; int dev; int64_t n; };
+  static std::mutex mu;
+  static Entry cache[64];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  for (int e = 0; e < used; ++e)
+    if (cache[e].k == k && cache[e].lds == lds && cache[e].dev == dev) return cache[e].n;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k), 256, lds) !=
+          hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
   }
-  return best;
+  const int64_t n = (int64_t)cus * per_cu;
+  if (used < 64) cache[used++] = Entry{k, lds, dev, n};
+  return n;
+}
+
+// Tile depth (2, 3 or 4 passes) for chunks of `chunk` rows; `kernel_for(np)`
+// gives the kernel of each depth, `grid` the workgroups of the launch.
+// Row slots past a chunk's end still issue their (redundant) loads, and on
+// this part the per-CU load path is what such slots cost, so among the
+// candidates the depth leaving the fewest empty slots wins, ties going to the
+// deeper tile.  A chunk that fits in three tiles at some depth has every tile
+// in flight at once: the candidates are those depths.  Longer chunks stream
+// through the two-buffer loop, where a grid that is resident all at once
+// measured faster than a deeper tile (1024 workgroups of 300-row chunks, four
+// query heads a kv head: 2 passes at 121 VGPRs, 4 workgroups a CU, 5-7 %
+// faster than 3 or 4 passes at 3 or 2): the candidates are the depths whose
+// kernel holds the whole grid at once, or all depths if none does.
+template <typename KernelFor>
+static int tile_depth(int chunk, int rows_per_pass, int64_t grid, size_t lds, KernelFor kernel_for) {
+  auto pick = [&](auto ok) {
+    int best = 0;
+    int64_t best_slots = INT64_MAX;
+    for (int np = 4; np >= 2; --np) {
+      const int64_t tile = (int64_t)np * rows_per_pass;
+      const int64_t slots = (chunk + tile - 1) / tile * tile;
+      if (ok(np, slots / tile) && slots < best_slots) {
+        best_slots = slots;
+        best = np;
+      }
+    }
+    return best;
+  };
+  int np = pick([](int, int64_t tiles) { return tiles <= 3; });
+  if (np) return np;
+  np = pick([&](int d, int64_t) { return resident_blocks(kernel_for(d), lds) >= grid; });
+  if (np) return np;
+  return pick([](int, int64_t) { return true; });
 }
 
 // Longest chunk one workgroup takes: its row offsets live in LDS (8 B each).
@@ -781,12 +824,14 @@ template <int FORM>
 static int launch_decode(const DecodeArgs& a, da_dtype dtype, int head_dim, void* stream) {
   const int esz = dtype == DA_BF16 ? 2 : 4;
   const int chunk = a.split < a.cap ? a.split : a.cap;
-  const int np = tile_depth(chunk, 256 / (head_dim * esz / 16));
+  const int64_t blocks = int64_t(a.n_q) * a.hkv * a.max_split;
+  const size_t lds = (size_t)chunk * sizeof(int64_t);
+  const int np = tile_depth(chunk, 256 / (head_dim * esz / 16), blocks, lds, [&](int d) {
+    return pick_kernel<FORM>(dtype, head_dim, a.hq / a.hkv, d);
+  });
   const decode_fn dk = pick_kernel<FORM>(dtype, head_dim, a.hq / a.hkv, np);
   const merge_fn mk = dtype == DA_BF16 ? (head_dim == 64 ? merge_kernel<true, 64> : merge_kernel<true, 128>)
                                        : (head_dim == 64 ? merge_kernel<false, 64> : merge_kernel<false, 128>);
-  const int64_t blocks = int64_t(a.n_q) * a.hkv * a.max_split;
-  const size_t lds = (size_t)chunk * sizeof(int64_t);
   hipLaunchKernelGGL(dk, dim3((unsigned)blocks), dim3(256), lds, (hipStream_t)stream, a);
   int rc = check_launch("decode_kernel");
   if (rc || a.max_split <= 1) return rc;
