@@ -17,13 +17,18 @@
 // transposed, O^T += V^T P^T (A = V^T by transposing LDS reads of row-major
 // V), so the online rescale is one multiply per lane register.
 //
-// Sparsity: only listed key tiles are visited.  Inside one, a wave whose
-// blocks are all wholly kept applies no mask; otherwise each row gets a
-// 64-bit keep word over the tile's keys (causal, prompt and window bits)
-// and every score keeps its bit or becomes -inf.  Workgroups are numbered so
-// that all query tiles of one (batch, head) share an XCD (hardware deals
-// workgroups to the 8 XCDs round-robin), which keeps the prompt keys/values
-// every tile re-reads in that XCD's L2.
+// Sparsity: only listed key tiles are visited.  Inside one, a wave none of
+// whose rows keeps a key of the tile only takes part in the copies and
+// barriers; a wave whose blocks are all wholly kept applies no mask;
+// otherwise each row gets a 64-bit keep word over the tile's keys (causal,
+// prompt and window bits) and every score keeps its bit or becomes -inf.
+// (Skipping single 16x16 blocks inside a wave behind uniform branches
+// measured slower: it breaks the interleaving of the unrolled products.)
+// Workgroups are numbered so that all query tiles of one (batch, head)
+// share an XCD (hardware deals workgroups to the 8 XCDs round-robin), which
+// keeps the prompt keys/values every tile re-reads in that XCD's L2, and so
+// that the last query tiles -- the longest under a causal mask -- start
+// first.
 #include "common.h"
 
 #include <type_traits>
@@ -220,8 +225,10 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   // row-diagonal band pattern: bit c of bp[r] says whether a key c places
   // before a query at residue r (mod G) lies within B of a multiple of G
   __shared__ uint64_t bp[MODE == DA_MODE_ROWDIAG ? GMAX : 1];
-  // this query tile's list: (key tile, full-block bits of waves 0..3); read
-  // from LDS so that no list read waits behind the tile DMA in flight
+  // this query tile's list, read from LDS so that no list read waits behind
+  // the tile DMA in flight: x = key tile | (wave w's blocks all wholly kept)
+  // << (16 + w), y = the need bits (8 per wave: row block rb, key block kq at
+  // bit 8w + 4rb + kq -- the block holds a kept pair)
   __shared__ int2 tl[MAX_LIST];
 
   const int t = threadIdx.x;
@@ -231,8 +238,11 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   const int lg = lane >> 4;
 
   const int n_bh = a.batch * a.heads;
-  const int bh = blockIdx.x % n_bh;    // all query tiles of (b, h) on one XCD
-  const int qt = blockIdx.x / n_bh;
+  // all query tiles of (b, h) on one XCD; the last (longest: most listed
+  // key tiles under a causal mask) query tiles start first, so the short
+  // ones fill in at the end of the grid
+  const int bh = blockIdx.x % n_bh;
+  const int qt = a.n_qt - 1 - (int)(blockIdx.x / n_bh);
   const int b = bh / a.heads;
   const int h = bh % a.heads;
   const int hk = h / (a.heads / a.kv_heads);
@@ -296,11 +306,14 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   for (int e = t; e < cnt; e += NTHREADS) {
     const int4 e0 = list[2 * e];
     const int4 e1 = list[2 * e + 1];
-    tl[e] = make_int2(clampi(e0.x, 0, jt_max), e1.x);
+    int allfull = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) allfull |= (((uint32_t)e1.x >> (8 * w)) & 0xffu) == 0xffu ? 1 << w : 0;
+    tl[e] = make_int2(clampi(e0.x, 0, jt_max) | (allfull << 16), e0.y);
   }
   __syncthreads();
 
-  issue(tl[0].x, 0);
+  issue(tl[0].x & 0xffff, 0);
 
   if constexpr (MODE == DA_MODE_ROWDIAG) {
     // band centres of residue r within reach of bits 0..63: r - kG for
@@ -414,14 +427,18 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
       __builtin_amdgcn_s_barrier();               // everyone's part; step idx-1 done
       __asm__ volatile("" ::: "memory");
     }
-    if (idx + 1 < cnt) issue(tl[idx + 1].x, (ST + 1) % NS);
+    if (idx + 1 < cnt) issue(tl[idx + 1].x & 0xffff, (ST + 1) % NS);
     const int2 e0 = tl[idx];
-    const unsigned full0 = ((uint32_t)e0.y >> (wave * 8)) & 0xffu;
+    const unsigned need8 = ((uint32_t)e0.y >> (wave * 8)) & 0xffu;
+    // a wave without a kept pair in this tile only takes part in the copies
+    // and barriers
+    if (need8 == 0) return;
+    const bool allfull = (e0.x >> (16 + wave)) & 1;
     const uint16_t* st0 = ring + ST * 2 * TILE;
 
     f32x4 sc[RB][4];
     scores_into(st0, sc);
-    if (full0 != 0xffu) apply_mask(sc, e0.x * BN);
+    if (!allfull) apply_mask(sc, (e0.x & 0xffff) * BN);
 
     float mts[RB];
     bool grow = false;
