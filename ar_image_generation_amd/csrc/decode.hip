@@ -181,6 +181,62 @@ __device__ inline int64_t row_offset(const DecodeArgs& a, const int32_t* bt, int
   return (int64_t)sq * a.page_stride + (int64_t)j * a.slot_stride;
 }
 
+// A query's keep-set in closed form (mask form of the decode kernel).
+// Entries 0 .. Pc-1 are the prompt positions (DENSE: every position up to
+// the query); the window entries follow in ascending position, i.e. in
+// descending offset d = i - j over the kept offsets in [0, dmax], dmax =
+// i - max(i - W, Pc).  The kept offsets are, for the band rule, 0 .. B,
+// and for the row-diagonal rule those within B of a multiple of G: exactly
+// the d with (d + B) mod G <= 2B -- runs of 2B + 1 offsets, period G, the
+// first starting at -B -- or every offset when 2B + 1 >= G.  So the count of
+// kept offsets in [0, x] is, with y = x + B, (y div G)(2B + 1) + min(y mod G,
+// 2B) + 1 - B, and the m-th kept offset (1-based, ascending) is
+// ((m + B - 1) div (2B + 1)) G + (m + B - 1) mod (2B + 1) - B.
+struct KeepCF {
+  int i, Pc, T;        // query position, prompt entries, window entries
+  int periodic;        // 1: row-diagonal runs; 0: offsets 0 .. T-1 all kept
+  uint32_t B, G, run;  // run = 2B + 1
+
+  __device__ int size() const { return Pc + T; }
+  // position of entry e, 0 <= e < size()
+  __device__ int entry(int e) const {
+    if (e < Pc) return e;
+    const uint32_t m = (uint32_t)(T - (e - Pc));   // 1-based ascending rank of the offset
+    if (!periodic) return i - (int)(m - 1);
+    const uint32_t nn = m + B - 1;
+    return i - (int)((nn / run) * G + nn % run - B);
+  }
+};
+
+__device__ inline KeepCF keep_cf(int mode, int i, int P, int W, int B, int G, bool bad) {
+  KeepCF k{};
+  k.i = i;
+  if (bad) return k;
+  const int L = i + 1;
+  if (mode == DA_MODE_DENSE) {
+    k.Pc = L;
+    return k;
+  }
+  k.Pc = P < L ? P : L;
+  const int wlo = i - W > k.Pc ? i - W : k.Pc;
+  const int dmax = i - wlo;                  // -1: the prompt reaches the query
+  if (dmax < 0) return k;
+  if (mode == DA_MODE_BAND) {
+    k.T = (dmax < B ? dmax : B) + 1;
+  } else if (2 * (int64_t)B + 1 >= G) {
+    k.T = dmax + 1;
+  } else {
+    k.periodic = 1;
+    k.B = (uint32_t)B;
+    k.G = (uint32_t)G;
+    k.run = 2 * (uint32_t)B + 1;
+    const uint32_t y = (uint32_t)dmax + (uint32_t)B;
+    const uint32_t ym = y % k.G;
+    k.T = (int)((y / k.G) * k.run + (ym < 2 * k.B ? ym : 2 * k.B) + 1 - k.B);
+  }
+  return k;
+}
+
 // FORM: 0 = listed keys; 1 = keep-set from the mask; 2 = from the mask with
 // a window and band per kv head.
 template <bool BF16, int HD, int GRP, int NP, int FORM>
@@ -227,21 +283,23 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const char* kb = reinterpret_cast<const char*>(a.k) + ((int64_t)g * a.head_stride + c * EPL) * ES;
   const char* vb = reinterpret_cast<const char*>(a.v) + ((int64_t)g * a.head_stride + c * EPL) * ES;
   TL b0, b1;
-  // mask form: chunk rows below pe are prompt entries loaded before the
-  // scan (pe = 0: none); sub_row is the chunk row of the appended token, or -1
-  int pe = 0, sub_row = -1;
+  // mask form: the chunk row of the appended token, or -1; the keep-set's
+  // closed form
+  int sub_row = -1;
+  KeepCF kc{};
   __shared__ u32x4 newrow[2 * LPR];       // mask form, KV append: the new K, V rows
-  // prompt rows of tile tt, issued before the keep-set scan so that their
-  // loads overlap it (the other lanes' slots are filled after the scan)
-  auto load_prompt = [&](TL& b, int tt) {
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int r = tt * ROWS + p * RPP + rsub;
-      if (r < pe) {
-        const int64_t o = row_offset(a, bt, sq, r0 + r);
-        b.k[p] = *reinterpret_cast<const u32x4*>(kb + o * ES);
-        b.v[p] = *reinterpret_cast<const u32x4*>(vb + o * ES);
-      }
+  // mask form: keep-set size; KV append state (the new rows travel in nkv)
+  int n_keep = 0, qpos = 0;
+  bool appending = false, stores = false;
+  u32x4 nkv = u32x4{0u, 0u, 0u, 0u};
+  // KV append: lanes 0 .. 2 LPR-1 store the new K / V row at position qpos
+  // (positions outside the cache are not written).  This workgroup's own
+  // use of the row reads the LDS copy, so no load has to wait for the store.
+  auto store_new_row = [&]() {
+    if (t < 2 * LPR) {
+      const int64_t o = row_offset(a, bt, sq, qpos);
+      char* base = reinterpret_cast<char*>(const_cast<void*>(t < LPR ? a.k : a.v));
+      *reinterpret_cast<u32x4*>(base + ((int64_t)g * a.head_stride + c * EPL + o) * ES) = nkv;
     }
   };
   if constexpr (!MASKED) {
@@ -297,21 +355,17 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     }
     __syncthreads();
   } else {
-    // ---- keep-set in the kernel: the same rule and order as the list
-    // builder.  Entries 0 .. Pc-1 are the prompt (or, DENSE, every key up to
-    // the query), offsets known without the scan.  The window [wlo, whi]
-    // follows, scanned 256 positions a round with a ballot per wave and a
-    // prefix over the four waves.  Every entry of this chunk not loaded yet
-    // gets its row offset in LDS; with list outputs, the kv-head-0
+    // ---- keep-set in the kernel, in closed form: entry e of the query's
+    // keep-set is e itself for the prompt part (or, DENSE, every key up to
+    // the query) and the (T - (e - Pc))-th kept offset d counted from the
+    // query for the window part (keep_cf), so every lane computes the
+    // positions of its own rows with no scan, barrier or memory read: the
+    // same entries in the same order as the list builder's scan.  With a
+    // contiguous cache every K/V load of the chunk is issued right after the
+    // query's position, prompt length and request arrive; a paged cache
+    // first reads the block-table entries of the chunk's rows (one round
+    // trip) into LDS row offsets.  With list outputs the kv-head-0
     // workgroups also write the entries of their chunk.
-    //
-    // A short chunk (at most three tiles, so every tile is in flight at
-    // once) of a contiguous cache loads the prompt rows of its first two
-    // tiles before the scan: their addresses need no memory read, and the
-    // scan's LDS-only barriers leave the loads in flight.  A paged cache
-    // would need block-table reads after them, and every such read waits
-    // for all earlier loads; long chunks stream in the two-buffer loop.
-    __shared__ int wcount[4];
     const int i = a.pos[qi];
     const int P = a.prompt[qi];
     const int sq_raw = a.seq[qi];
@@ -323,8 +377,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     }
     // KV append: lanes 0 .. LPR-1 carry the new token's K chunk of this kv
     // head, lanes LPR .. 2 LPR-1 its V chunk
-    const bool appending = a.k_new != nullptr;
-    u32x4 nkv = u32x4{0u, 0u, 0u, 0u};
+    appending = a.k_new != nullptr;
     if (appending && t < 2 * LPR) {
       const void* src = t < LPR ? a.k_new : a.v_new;
       const int64_t off = ((int64_t)qi * a.hkv + g) * HD + c * EPL;
@@ -336,82 +389,44 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     off0 = bt ? (int64_t)clampi(bt[0], 0, a.n_pages - 1) * a.page_stride
               : (int64_t)sq * a.page_stride;
     const bool bad = i < 0 || P < 0;
-    // KV append: lanes 0 .. 2 LPR-1 store the new K / V row at position i
-    // (positions outside the cache are not written).  This workgroup's own
-    // use of the row reads the LDS copy, so no load has to wait for the store.
-    const bool stores = appending && !bad && i < a.max_len;
-    auto store_new_row = [&]() {
-      if (t < 2 * LPR) {
-        const int64_t o = row_offset(a, bt, sq, i);
-        char* base = reinterpret_cast<char*>(const_cast<void*>(t < LPR ? a.k : a.v));
-        *reinterpret_cast<u32x4*>(base + ((int64_t)g * a.head_stride + c * EPL + o) * ES) = nkv;
-      }
-    };
-    if (stores && a.max_split == 1) store_new_row();
-    if (appending && t < 2 * LPR) newrow[t] = nkv;
-    const int L = i + 1;
-    int Pc = 0, wlo = 1, whi = 0;
-    if (!bad) {
-      if (a.mode == DA_MODE_DENSE) {
-        Pc = L;
-      } else {
-        Pc = P < L ? P : L;
-        wlo = i - Wm > Pc ? i - Wm : Pc;
-        whi = i;
-      }
-    }
-    const int lim_e = r0 + lim;                       // entries of this chunk: [r0, lim_e)
-    const int pc_e = clampi(Pc - r0, 0, lim);        // prompt entries of this chunk
-    if (!bt && lim <= 3 * ROWS) {
-      pe = pc_e;
-      load_prompt(b0, 0);
-      load_prompt(b1, 1);
-    }
-    const bool lists = a.count_out != nullptr && g == 0;
-    int32_t* my_out = lists ? a.idx_out + (int64_t)qi * a.cap : nullptr;
-    for (int r = t; r < pc_e; r += 256) {
-      if (r >= pe) rowoff[r] = row_offset(a, bt, sq, r0 + r);
-      if (lists) my_out[r0 + r] = r0 + r;
-    }
-    const int wave_id = t >> 6;
-    const int lane = t & 63;
-    const uint64_t below = (uint64_t(1) << lane) - 1;
-    int n = Pc;
-    for (int base = wlo; base <= whi; base += 256) {
-      const int j = base + t;
-      const bool kp = j <= whi && window_keep(a.mode, i - j, Bm, a.G);
-      const uint64_t bal = __ballot(kp);
-      if (lane == 0) wcount[wave_id] = __popcll(bal);
-      lds_barrier();
-      int before = 0, total = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        before += w < wave_id ? wcount[w] : 0;
-        total += wcount[w];
-      }
-      const int r = n + before + __popcll(bal & below);
-      if (kp && r >= r0 && r < lim_e) {
-        rowoff[r - r0] = row_offset(a, bt, sq, j);
-        if (lists) my_out[r] = j;
-      }
-      n += total;
-      lds_barrier();                                  // wcount is reused
-    }
-    if (lists && s == 0 && t == 0) a.count_out[qi] = n;
-    if (a.ws_cnt && s == 0 && t == 0) a.ws_cnt[(int64_t)qi * a.hkv + g] = n;
+    qpos = i;
+    stores = appending && !bad && i < a.max_len;
+    kc = keep_cf(a.mode, i, P, Wm, Bm, a.G, bad);
+    const int n = kc.size();
+    n_keep = n;
     cnt = n < a.cap ? n : a.cap;
-    // KV append, several chunks: the chunk that attends the last entry
-    // (position i itself when the list is not truncated) stores the new row
-    if (stores && a.max_split > 1 && cnt > 0 && (cnt - 1) / a.split == s) store_new_row();
     // the new row is entry n - 1 of the keep-set (position i is always kept);
     // it is attended unless the list was cut at cap
-    if (stores && n <= a.cap && n - 1 >= r0 && n - 1 < lim_e) sub_row = n - 1 - r0;
-    lds_barrier();                                    // row offsets, new row copy
+    if (stores && n <= a.cap && n - 1 >= r0 && n - 1 < r0 + lim) sub_row = n - 1 - r0;
     if (r0 >= cnt) {
-      __builtin_amdgcn_s_waitcnt(0);                  // the prompt loads above are dropped
+      // nothing to attend; the lists, sizes and the appended row are still due
+      if (a.count_out != nullptr && g == 0 && s == 0 && t == 0) a.count_out[qi] = n;
+      if (a.ws_cnt && s == 0 && t == 0) a.ws_cnt[(int64_t)qi * a.hkv + g] = n;
+      if (stores && a.max_split == 1) store_new_row();
       return;
     }
     nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
+    if (bt) {
+      // ---- stage 1 (paged): element offset of every row of the chunk
+      for (int base = 0; base < nrows; base += IPT * 256) {
+        int jj[IPT], pg[IPT];
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) {
+          const int r = base + u * 256 + t;
+          jj[u] = clampi(kc.entry(r0 + (r < nrows ? r : nrows - 1)), 0, a.max_len - 1);
+        }
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) pg[u] = bt[jj[u] >> a.ps_shift];
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) {
+          const int r = base + u * 256 + t;
+          if (r < nrows)
+            rowoff[r] = (int64_t)clampi(pg[u], 0, a.n_pages - 1) * a.page_stride +
+                        (int64_t)(jj[u] & a.ps_mask) * a.slot_stride;
+        }
+      }
+      __syncthreads();
+    }
   }
 
   // ---- query slices as fp32 (the fp32 path; bf16 uses the packed words)
@@ -488,53 +503,69 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     }
   };
 
-  if (MASKED && pe > 0) {
-    // prompt rows of tiles 0 and 1 are in flight: the rest of those two
-    // tiles (window rows from LDS, slots past the chunk position 0's row),
-    // then tile 2 (prompt rows direct); nt <= 3 here
-    auto load_rest = [&](TL& b, int tt) {
+  // Row r of the chunk: its element offset from the keep-set's closed form
+  // (mask form, contiguous cache) or from LDS; slots past the chunk read
+  // the request's first row (always valid, and shared, so cache hits).
+  const bool direct = MASKED && bt == nullptr;
+  auto load = [&](TL& b, int tt) {
+    if (direct) {
       int64_t o[NP];
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
         const int r = tt * ROWS + p * RPP + rsub;
-        o[p] = rowoff[r < nrows ? r : nrows - 1];
-        o[p] = r < nrows ? o[p] : off0;
-        if (tt >= 2 && r < pe) o[p] = row_offset(a, bt, sq, r0 + r);
+        const int j = clampi(kc.entry(r0 + (r < nrows ? r : 0)), 0, a.max_len - 1);
+        o[p] = r < nrows ? (int64_t)sq * a.page_stride + (int64_t)j * a.slot_stride : off0;
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        const int r = tt * ROWS + p * RPP + rsub;
-        if (tt >= 2 || r >= pe) {
-          b.k[p] = *reinterpret_cast<const u32x4*>(kb + o[p] * ES);
-          b.v[p] = *reinterpret_cast<const u32x4*>(vb + o[p] * ES);
-        }
+        b.k[p] = *reinterpret_cast<const u32x4*>(kb + o[p] * ES);
+        b.v[p] = *reinterpret_cast<const u32x4*>(vb + o[p] * ES);
       }
-    };
-    TL b2;
-    load_rest(b0, 0);
-    load_rest(b1, 1);
-    load_rest(b2, 2);
-    process(b0, 0);
-    if (nt > 1) process(b1, 1);
-    if (nt > 2) process(b2, 2);
-  } else if (nt <= 3) {
+    } else {
+      b.load(kb, vb, rowoff, off0, tt, rsub, nrows);
+    }
+  };
+  // mask form: work that no load waits for, done once the first loads are
+  // in flight -- list outputs, keep-set sizes for the merge, the appended
+  // row's store and its LDS copy
+  auto after_issue = [&]() {
+    if constexpr (MASKED) {
+      const int lim_e = r0 + lim;                     // entries of this chunk: [r0, lim_e)
+      if (a.count_out != nullptr && g == 0) {
+        int32_t* my_out = a.idx_out + (int64_t)qi * a.cap;
+        const int hi = n_keep < lim_e ? n_keep : lim_e;
+        for (int e = r0 + t; e < hi; e += 256) my_out[e] = kc.entry(e);
+        if (s == 0 && t == 0) a.count_out[qi] = n_keep;
+      }
+      if (a.ws_cnt && s == 0 && t == 0) a.ws_cnt[(int64_t)qi * a.hkv + g] = n_keep;
+      // KV append: one chunk -- this one -- or, with several, the chunk that
+      // attends the last entry (position i itself when the list is not cut)
+      if (stores && (a.max_split == 1 || (cnt - 1) / a.split == s)) store_new_row();
+      if (appending) {
+        if (t < 2 * LPR) newrow[t] = nkv;
+        lds_barrier();
+      }
+    }
+  };
+  if (nt <= 3) {
     // short chunk: every tile in flight at once, none loaded past the end
     // (the two-buffer loop below always issues one tile of lookahead)
     TL b2;
-    b0.load(kb, vb, rowoff, off0, 0, rsub, nrows);
-    b1.load(kb, vb, rowoff, off0, 1, rsub, nrows);
-    b2.load(kb, vb, rowoff, off0, 2, rsub, nrows);
+    load(b0, 0);
+    load(b1, 1);
+    load(b2, 2);
+    after_issue();
     process(b0, 0);
     if (nt > 1) process(b1, 1);
     if (nt > 2) process(b2, 2);
   } else {
-    b0.load(kb, vb, rowoff, off0, 0, rsub, nrows);
+    load(b0, 0);
+    after_issue();
     for (int tt = 0; tt < nt; tt += 2) {
-      b1.load(kb, vb, rowoff, off0, tt + 1, rsub, nrows);
+      load(b1, tt + 1);
       process(b0, tt);
       if (tt + 1 >= nt) break;
-      b0.load(kb, vb, rowoff, off0, tt + 2, rsub, nrows);
+      load(b0, tt + 2);
       process(b1, tt + 1);
     }
   }
@@ -825,7 +856,8 @@ static int launch_decode(const DecodeArgs& a, da_dtype dtype, int head_dim, void
   const int esz = dtype == DA_BF16 ? 2 : 4;
   const int chunk = a.split < a.cap ? a.split : a.cap;
   const int64_t blocks = int64_t(a.n_q) * a.hkv * a.max_split;
-  const size_t lds = (size_t)chunk * sizeof(int64_t);
+  // row offsets in LDS: every list, and the mask form of a paged cache
+  const size_t lds = FORM >= 1 && !a.block_table ? 0 : (size_t)chunk * sizeof(int64_t);
   const int np = tile_depth(chunk, 256 / (head_dim * esz / 16), blocks, lds, [&](int d) {
     return pick_kernel<FORM>(dtype, head_dim, a.hq / a.hkv, d);
   });
