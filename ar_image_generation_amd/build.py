@@ -27,6 +27,9 @@ FLAGS = [
     # no packed-fp32 instructions in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
+    # the first kernel arguments arrive preloaded in SGPRs (gfx950 kernel-
+    # argument preloading); kernels read the rest from the argument block
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", os.path.join(ROOT, "include"),
 ]
 

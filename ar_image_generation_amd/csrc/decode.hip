@@ -240,7 +240,18 @@ __device__ inline KeepCF keep_cf(int mode, int i, int P, int W, int B, int G, bo
 // FORM: 0 = listed keys; 1 = keep-set from the mask; 2 = from the mask with
 // a window and band per kv head.
 template <bool BF16, int HD, int GRP, int NP, int FORM>
-__global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
+//
+// The arguments a workgroup needs before its first memory reads -- the
+// query's position, prompt length and request arrays, q, K, V and the grid
+// decomposition -- come first and one by one, so that they fit the 16
+// kernel-argument SGPRs the hardware can preload at launch (the library is
+// built with kernel-argument preloading): the position/request reads then
+// start without first waiting for the argument block.  The full argument
+// block follows; its loads overlap those reads.
+__global__ void __launch_bounds__(256) decode_kernel(const int32_t* pos_p, const int32_t* prompt_p,
+                                                     const int32_t* seq_p, int hkv_p, int max_split_p,
+                                                     const void* q_p, const void* k_p, const void* v_p,
+                                                     DecodeArgs a) {
   constexpr bool MASKED = FORM >= 1;
   constexpr bool PERHEAD = FORM == 2;
   using TL = Tile<BF16, HD, NP>;
@@ -261,10 +272,23 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
   const int rsub = t / LPR;
 
   const int bid = blockIdx.x;
-  const int s = bid % a.max_split;
-  const int qg = bid / a.max_split;
-  const int qi = qg / a.hkv;
-  const int g = qg % a.hkv;
+  const int s = bid % max_split_p;
+  const int qg = bid / max_split_p;
+  const int qi = qg / hkv_p;
+  const int g = qg % hkv_p;
+  // mask form: the query's position, prompt length and request, read first
+  // and together (the empty asm keeps later memory operations, and the
+  // waits they bring, behind these three reads)
+  int i_m = 0, P_m = 0, sq_m = 0;
+  if constexpr (MASKED) {
+    i_m = pos_p[qi];
+    P_m = prompt_p[qi];
+    sq_m = seq_p[qi];
+    // the argument-block fields the first addresses need, read alongside
+    __asm__ volatile("" ::"s"(a.split), "s"(a.cap), "s"(a.hq), "s"(a.head_stride), "s"(a.page_stride),
+                     "s"(a.slot_stride), "s"(a.n_seq), "s"(a.max_len), "s"(a.mode), "s"(a.W), "s"(a.B),
+                     "s"(a.G) : "memory");
+  }
   const int r0 = s * a.split;
   const int lim = a.cap - r0 < a.split ? a.cap - r0 : a.split;   // >= 1
 
@@ -274,14 +298,14 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
     const int64_t qoff = ((int64_t)qi * a.hq + g * GRP + h) * HD + c * EPL;
-    qw[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.q) + qoff * ES);
+    qw[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(q_p) + qoff * ES);
   }
   constexpr int IPT = 4;                  // list entries per thread per round
   int cnt, nrows, sq;
   const int32_t* bt;
   int64_t off0;
-  const char* kb = reinterpret_cast<const char*>(a.k) + ((int64_t)g * a.head_stride + c * EPL) * ES;
-  const char* vb = reinterpret_cast<const char*>(a.v) + ((int64_t)g * a.head_stride + c * EPL) * ES;
+  const char* kb = reinterpret_cast<const char*>(k_p) + ((int64_t)g * a.head_stride + c * EPL) * ES;
+  const char* vb = reinterpret_cast<const char*>(v_p) + ((int64_t)g * a.head_stride + c * EPL) * ES;
   TL b0, b1;
   // mask form: the chunk row of the appended token, or -1; the keep-set's
   // closed form
@@ -311,7 +335,7 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
       jj[u] = myidx[r < lim ? r : lim - 1];
     }
     cnt = a.count[qi];
-    const int sq_raw = a.seq[qi];
+    const int sq_raw = seq_p[qi];
     // compiler-only barrier: keeps the loads above ahead of the count test
     // (they would otherwise be sunk behind it); emits nothing
     __asm__ volatile("" ::: "memory");
@@ -366,9 +390,9 @@ __global__ void __launch_bounds__(256) decode_kernel(DecodeArgs a) {
     // first reads the block-table entries of the chunk's rows (one round
     // trip) into LDS row offsets.  With list outputs the kv-head-0
     // workgroups also write the entries of their chunk.
-    const int i = a.pos[qi];
-    const int P = a.prompt[qi];
-    const int sq_raw = a.seq[qi];
+    const int i = i_m;
+    const int P = P_m;
+    const int sq_raw = sq_m;
     // the mask's window and band, or this kv head's own (negative read as 0)
     int Wm = a.W, Bm = a.B;
     if constexpr (PERHEAD) {
@@ -683,7 +707,8 @@ __global__ void __launch_bounds__(64) merge_kernel(DecodeArgs a) {
   if (a.lse && lane == 0) a.lse[row] = (M + log2f(L)) * kLn2;
 }
 
-typedef void (*decode_fn)(DecodeArgs);
+typedef void (*decode_fn)(const int32_t*, const int32_t*, const int32_t*, int, int, const void*,
+                          const void*, const void*, DecodeArgs);
 typedef void (*merge_fn)(DecodeArgs);
 
 // Tile depth: NP passes per tile (two tiles in flight per workgroup).
@@ -864,7 +889,8 @@ static int launch_decode(const DecodeArgs& a, da_dtype dtype, int head_dim, void
   const decode_fn dk = pick_kernel<FORM>(dtype, head_dim, a.hq / a.hkv, np);
   const merge_fn mk = dtype == DA_BF16 ? (head_dim == 64 ? merge_kernel<true, 64> : merge_kernel<true, 128>)
                                        : (head_dim == 64 ? merge_kernel<false, 64> : merge_kernel<false, 128>);
-  hipLaunchKernelGGL(dk, dim3((unsigned)blocks), dim3(256), lds, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(dk, dim3((unsigned)blocks), dim3(256), lds, (hipStream_t)stream, a.pos, a.prompt,
+                     a.seq, a.hkv, a.max_split, a.q, a.k, a.v, a);
   int rc = check_launch("decode_kernel");
   if (rc || a.max_split <= 1) return rc;
   hipLaunchKernelGGL(mk, dim3((unsigned)(int64_t(a.n_q) * a.hq)), dim3(64), 0, (hipStream_t)stream, a);
