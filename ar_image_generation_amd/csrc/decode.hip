@@ -242,16 +242,17 @@ __device__ inline KeepCF keep_cf(int mode, int i, int P, int W, int B, int G, bo
 template <bool BF16, int HD, int GRP, int NP, int FORM>
 //
 // The arguments a workgroup needs before its first memory reads -- the
-// query's position, prompt length and request arrays, q, K, V and the grid
-// decomposition -- come first and one by one, so that they fit the 16
-// kernel-argument SGPRs the hardware can preload at launch (the library is
-// built with kernel-argument preloading): the position/request reads then
-// start without first waiting for the argument block.  The full argument
-// block follows; its loads overlap those reads.
-__global__ void __launch_bounds__(256) decode_kernel(const int32_t* pos_p, const int32_t* prompt_p,
+// query's position and prompt length arrays (list form: the counts and the
+// lists), its request array, the grid decomposition, K, V and q -- come
+// first and one by one; all but q fit the 14 kernel-argument SGPRs the
+// hardware preloads at launch (the library is built with kernel-argument
+// preloading), so the position/request reads start without first waiting
+// for the argument block.  The full argument block follows; its loads
+// overlap those reads.
+__global__ void __launch_bounds__(256) decode_kernel(const int32_t* m0_p, const int32_t* m1_p,
                                                      const int32_t* seq_p, int hkv_p, int max_split_p,
-                                                     const void* q_p, const void* k_p, const void* v_p,
-                                                     DecodeArgs a) {
+                                                     int cap_p, int split_p, const void* k_p,
+                                                     const void* v_p, const void* q_p, DecodeArgs a) {
   constexpr bool MASKED = FORM >= 1;
   constexpr bool PERHEAD = FORM == 2;
   using TL = Tile<BF16, HD, NP>;
@@ -281,23 +282,23 @@ __global__ void __launch_bounds__(256) decode_kernel(const int32_t* pos_p, const
   // waits they bring, behind these three reads)
   int i_m = 0, P_m = 0, sq_m = 0;
   if constexpr (MASKED) {
-    i_m = pos_p[qi];
-    P_m = prompt_p[qi];
+    i_m = m0_p[qi];
+    P_m = m1_p[qi];
     sq_m = seq_p[qi];
     // the argument-block fields the first addresses need, read alongside
-    __asm__ volatile("" ::"s"(a.split), "s"(a.cap), "s"(a.hq), "s"(a.head_stride), "s"(a.page_stride),
+    __asm__ volatile("" ::"s"(a.head_stride), "s"(a.page_stride),
                      "s"(a.slot_stride), "s"(a.n_seq), "s"(a.max_len), "s"(a.mode), "s"(a.W), "s"(a.B),
                      "s"(a.G) : "memory");
   }
-  const int r0 = s * a.split;
-  const int lim = a.cap - r0 < a.split ? a.cap - r0 : a.split;   // >= 1
+  const int r0 = s * split_p;
+  const int lim = cap_p - r0 < split_p ? cap_p - r0 : split_p;   // >= 1
 
   // ---- stage 0: query slices, list entries, count and request in one
   // round trip (every load unconditional and in bounds)
   u32x4 qw[GRP];
 #pragma unroll
   for (int h = 0; h < GRP; ++h) {
-    const int64_t qoff = ((int64_t)qi * a.hq + g * GRP + h) * HD + c * EPL;
+    const int64_t qoff = (((int64_t)qi * hkv_p + g) * GRP + h) * HD + c * EPL;   // hq = hkv GRP
     qw[h] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(q_p) + qoff * ES);
   }
   constexpr int IPT = 4;                  // list entries per thread per round
@@ -327,18 +328,20 @@ __global__ void __launch_bounds__(256) decode_kernel(const int32_t* pos_p, const
     }
   };
   if constexpr (!MASKED) {
-    const int32_t* myidx = a.idx + (int64_t)qi * a.cap + r0;
+    const int32_t* myidx = m1_p + (int64_t)qi * cap_p + r0;
     int jj[IPT];
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
       const int r = u * 256 + t;
       jj[u] = myidx[r < lim ? r : lim - 1];
     }
-    cnt = a.count[qi];
+    cnt = m0_p[qi];
     const int sq_raw = seq_p[qi];
     // compiler-only barrier: keeps the loads above ahead of the count test
-    // (they would otherwise be sunk behind it); emits nothing
-    __asm__ volatile("" ::: "memory");
+    // (they would otherwise be sunk behind it), with the argument-block
+    // fields the row offsets need read alongside; emits nothing
+    __asm__ volatile("" ::"s"(a.head_stride), "s"(a.page_stride), "s"(a.slot_stride), "s"(a.n_seq),
+                     "s"(a.max_len) : "memory");
     cnt = cnt < a.cap ? cnt : a.cap;
     if (r0 >= cnt) return;
     nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
@@ -707,8 +710,8 @@ __global__ void __launch_bounds__(64) merge_kernel(DecodeArgs a) {
   if (a.lse && lane == 0) a.lse[row] = (M + log2f(L)) * kLn2;
 }
 
-typedef void (*decode_fn)(const int32_t*, const int32_t*, const int32_t*, int, int, const void*,
-                          const void*, const void*, DecodeArgs);
+typedef void (*decode_fn)(const int32_t*, const int32_t*, const int32_t*, int, int, int, int,
+                          const void*, const void*, const void*, DecodeArgs);  // ..., k, v, q, args
 typedef void (*merge_fn)(DecodeArgs);
 
 // Tile depth: NP passes per tile (two tiles in flight per workgroup).
@@ -889,8 +892,10 @@ static int launch_decode(const DecodeArgs& a, da_dtype dtype, int head_dim, void
   const decode_fn dk = pick_kernel<FORM>(dtype, head_dim, a.hq / a.hkv, np);
   const merge_fn mk = dtype == DA_BF16 ? (head_dim == 64 ? merge_kernel<true, 64> : merge_kernel<true, 128>)
                                        : (head_dim == 64 ? merge_kernel<false, 64> : merge_kernel<false, 128>);
-  hipLaunchKernelGGL(dk, dim3((unsigned)blocks), dim3(256), lds, (hipStream_t)stream, a.pos, a.prompt,
-                     a.seq, a.hkv, a.max_split, a.q, a.k, a.v, a);
+  const int32_t* m0 = FORM >= 1 ? a.pos : a.count;
+  const int32_t* m1 = FORM >= 1 ? a.prompt : a.idx;
+  hipLaunchKernelGGL(dk, dim3((unsigned)blocks), dim3(256), lds, (hipStream_t)stream, m0, m1, a.seq,
+                     a.hkv, a.max_split, a.cap, a.split, a.k, a.v, a.q, a);
   int rc = check_launch("decode_kernel");
   if (rc || a.max_split <= 1) return rc;
   hipLaunchKernelGGL(mk, dim3((unsigned)(int64_t(a.n_q) * a.hq)), dim3(64), 0, (hipStream_t)stream, a);
