@@ -121,6 +121,18 @@ def test_mask_parameters(W, B, G):
         assert_same(a, b, cap)
 
 
+@pytest.mark.parametrize("W,B,G", [(2**31 - 1, 3, 64), (96, 2**31 - 1, 32), (2**30, 2**30, 2**31 - 1),
+                                   (40, 7, 15), (2**31 - 1, 0, 2**31 - 1)])
+def test_extreme_mask_parameters(W, B, G):
+    """Window, band and grid width at the int32 limits, and 2B+1 = G: the
+    in-kernel keep-set (closed form) equals the list builder's (scan)."""
+    cfg = wl.small_decode("llamagen_b16", n_seq=2)
+    inp = wl.decode_inputs(cfg)
+    for mode in (O.BAND, O.ROWDIAG):
+        a, b, cap = both_paths(inp, mode, 4096, W=W, B=B, G=G)
+        assert_same(a, b, cap)
+
+
 def test_truncated_capacity():
     """cap below the keep-set size: both paths attend to the first cap
     entries and report the true count."""
