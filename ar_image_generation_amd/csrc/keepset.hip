@@ -23,12 +23,17 @@ struct KeepsetArgs {
   int32_t* runs;
 };
 
-__global__ void __launch_bounds__(256) keepset_kernel(KeepsetArgs a) {
+// The position and prompt-length arrays and the query count also come as
+// leading arguments, which the hardware preloads into SGPRs (the library is
+// built with kernel-argument preloading): a wave reads its query's position
+// and prompt length without first waiting for the argument block.
+__global__ void __launch_bounds__(256) keepset_kernel(const int32_t* pos, const int32_t* prompt, int n_q,
+                                                      KeepsetArgs a) {
   const int lane = threadIdx.x & 63;
   const int q = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (q >= a.n_q) return;
-  const int i = a.pos[q];
-  const int P = a.prompt[q];
+  if (q >= n_q) return;
+  const int i = pos[q];
+  const int P = prompt[q];
   const bool bad = i < 0 || P < 0 || (!a.causal && i >= a.n_keys);
   if (bad) {
     if (lane == 0) {
@@ -137,6 +142,6 @@ extern "C" int da_keepset_build(const da_mask* m, int32_t n_q, const int32_t* po
   a.n_runs = n_runs;
   a.runs = runs;
   const int blocks = (n_q + 3) / 4;
-  hipLaunchKernelGGL(keepset_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(keepset_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, a.pos, a.prompt, a.n_q, a);
   return check_launch("keepset_kernel");
 }
