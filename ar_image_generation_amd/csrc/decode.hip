@@ -24,12 +24,12 @@
 // needs agent-scope fences, which write back and invalidate the whole L2 of
 // the XCD on this part: measured far slower than a second launch.)
 //
-// Mask form (FORM 1, 2): instead of reading lists, each workgroup builds the
-// entries of its chunk from the query's position, prompt length and the
-// mask with the list builder's rule and order (prompt entries directly, the
-// window by a ballot scan), so keep-set build and attention are one launch;
-// the lists can be written out as well, and the new token's K/V rows can be
-// appended to the cache at its position before they are read.
+// Mask form (FORM 1, 2): instead of reading lists, every lane computes the
+// entries of its rows from the query's position, prompt length and the
+// mask -- the list builder's entries in the builder's order, from the
+// keep-set's closed form (KeepCF) -- so keep-set build and attention are one
+// launch; the lists can be written out as well, and the new token's K/V rows
+// can be appended to the cache at its position before they are read.
 //
 // Every index read from device memory (request, position, page) is clamped
 // into the cache extents the host passes, so no list content can make the
