@@ -143,13 +143,18 @@ def test_truncated_capacity():
     assert_same(a, b, cap)
 
 
-def test_full_llamagen_equals_list_path():
-    """The benchmark workload and launch setting."""
-    cfg = wl.CONFIGS["llamagen_b16"]
+@pytest.mark.parametrize("name", ["llamagen_b16", "gqa_b64", "paged_b128"])
+def test_full_size_equals_list_path(name):
+    """The decode workloads at full size in their launch setting (one chunk
+    per query and kv head), every mask mode they run plus the dense one:
+    the in-kernel keep-set equals the list path bitwise."""
+    cfg = wl.CONFIGS[name]
     inp = wl.decode_inputs(cfg)
-    a, b, cap = both_paths(inp, cfg.modes[0], cfg.split)
-    assert_same(a, b, cap)
-    assert torch.isfinite(b[0].float()).all()
+    for mode in dict.fromkeys(tuple(cfg.modes) + (O.DENSE,)):
+        split = cfg.dense_split if mode == O.DENSE else cfg.split
+        a, b, cap = both_paths(inp, mode, split)
+        assert_same(a, b, cap)
+        assert torch.isfinite(b[0].float()).all()
 
 
 def test_without_lists_same_output():
