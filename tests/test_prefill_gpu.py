@@ -143,3 +143,19 @@ def test_random_masks_and_shapes(seed):
     out, lse = run(q, k, v, prompt, mode, W, B, G)
     rows = [(b, h, i) for b in range(batch) for h in range(heads) for i in range(n)]
     check(out, lse, oracle_rows(q, k, v, prompt, mode, W, B, G, rows))
+
+
+@pytest.mark.parametrize("mode", [O.ROWDIAG, O.DENSE])
+def test_longest_sequence_sampled_rows(mode):
+    """The longest sequence the prefill takes (65536 tokens, its whole tile
+    list in LDS): sampled rows -- the first and last query tiles, tile
+    boundaries and seeded random rows -- against the oracle."""
+    n, P, W, B, G = 65536, 256, 256, 3, 64
+    q = randn((1, 1, n, 128), 11)
+    k = randn((1, 1, n, 128), 12)
+    v = randn((1, 1, n, 128), 13)
+    out, lse = run(q, k, v, [P], mode, W, B, G)
+    rng = np.random.default_rng(14)
+    pick = {0, 1, 127, 128, 255, 256, 257, n - 129, n - 128, n - 2, n - 1}
+    pick |= {int(x) for x in rng.integers(0, n, 16)}
+    check(out, lse, oracle_rows(q, k, v, [P], mode, W, B, G, [(0, 0, i) for i in sorted(pick)]))
