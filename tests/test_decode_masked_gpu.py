@@ -350,3 +350,38 @@ def test_per_head_masks(split):
                                                 want_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(o1.cpu(), o2.cpu()) and torch.equal(l1.cpu(), l2.cpu())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_long_context(dtype):
+    """Queries ~100k positions into their request (prompt 2000): the dense
+    keep-set spans 25 chunks of the longest split (4096) and the merge; the
+    row-diagonal one a single chunk.  Both paths against the oracle, and the
+    mask path bitwise against the list path."""
+    n_seq, hq, hkv, hd, L = 2, 4, 2, 128, 100_001
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(21)
+    k = torch.randn((n_seq, hkv, L, hd), generator=g).to(tdt)
+    v = torch.randn((n_seq, hkv, L, hd), generator=g).to(tdt)
+    q = torch.randn((3, hq, hd), generator=g).to(tdt)
+    pos = torch.tensor([100_000, 99_871, 65_537], dtype=torch.int32)
+    prompt = torch.tensor([2000, 2000, 17], dtype=torch.int32)
+    seq = torch.tensor([0, 1, 1], dtype=torch.int32)
+    kd, vd, qd = k.to(dev()), v.to(dev()), q.to(dev())
+    for mode, split in ((O.DENSE, 4096), (O.ROWDIAG, 4096)):
+        m = da.mask(mode, 256, 3, 64)
+        cap = da.keep_cap(m, int(pos.max()), int(prompt.max()))
+        count, idx, _, _ = da.keepset_build(m, pos.to(dev()), prompt.to(dev()), cap)
+        o1, l1 = da.sparse_decode_attn(qd, kd, vd, seq.to(dev()), count, idx, split=split, want_lse=True)
+        o2, l2, c2, i2 = da.sparse_decode_attn_masked(m, qd, kd, vd, seq.to(dev()), pos.to(dev()),
+                                                      prompt.to(dev()), cap=cap, split=split,
+                                                      want_lse=True, want_lists=True)
+        torch.cuda.synchronize()
+        assert torch.equal(count, c2) and torch.equal(o1, o2) and torch.equal(l1, l2)
+        for qi in range(3):
+            n = int(count[qi])
+            assert torch.equal(idx[qi, :n], i2[qi, :n])
+        ref_o, ref_l = O.decode_attention(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                          pos.numpy(), prompt.numpy(), seq.numpy(),
+                                          W=256, B=3, G=64, mode=mode)
+        assert_close(o2.cpu(), l2.cpu(), ref_o, ref_l, dtype)
