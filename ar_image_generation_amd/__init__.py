@@ -14,6 +14,7 @@ from .api import (  # noqa: F401
     keep_cap,
     keep_count,
     keepset_build,
+    keepset_tiles,
     kv_cache,
     mask,
     prefill_tiles_build,

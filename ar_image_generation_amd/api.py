@@ -46,7 +46,13 @@ def keep_count(m: DaMask, pos: int, prompt_len: int, n_keys: int = 0) -> int:
     return int(r)
 
 
-def keep_cap(m: DaMask, max_pos: int, max_prompt: int, n_keys: int = 0) -> int:
+def keep_cap(m: DaMask, max_pos: int, max_prompt: int, n_keys: int = 0, head_wb=None) -> int:
+    """Bound on keep-set sizes (sizes ``cap``).  With per-head masks
+    ``head_wb`` (host [hq, 2] (W, B) pairs), the bound of the widest head's
+    mask: a kv group reads the keep-set of its widest (W, B)."""
+    if head_wb is not None:
+        wb = [(max(int(w), 0), max(int(b), 0)) for w, b in head_wb]
+        m = DaMask(m.mode, max(w for w, _ in wb), max(b for _, b in wb), m.G, m.causal)
     r = load().da_keep_cap(m, max_pos, max_prompt, n_keys)
     check(0 if r >= 0 else int(r), "da_keep_cap")
     return int(r)
@@ -57,6 +63,24 @@ def keepset_build(m: DaMask, pos: torch.Tensor, prompt_len: torch.Tensor, cap: i
                   n_runs=None, runs=None):
     """Returns (count [n_q], idx [n_q, cap], n_runs [n_q] or None,
     runs [n_q, max_runs, 2] or None), all int32 on pos.device."""
+    return _keepset_build(m, pos, prompt_len, cap, n_keys, max_runs, count, idx, n_runs, runs,
+                          0, 0, None, None)[:4]
+
+
+def keepset_tiles(m: DaMask, pos: torch.Tensor, prompt_len: torch.Tensor, cap: int, tile: int,
+                  cap_tiles: int, n_keys: int = 0, tiles=None, n_tiles=None):
+    """keepset_build with the split-KV tile list: returns (count, idx,
+    tiles [cap_tiles, 2] int32 (query, first entry), n_tiles [1] int64)."""
+    if tile < 1:
+        raise ValueError("keepset_tiles: tile must be >= 1")
+    count, idx, _, _, tiles, n_tiles = _keepset_build(m, pos, prompt_len, cap, n_keys, 0, None,
+                                                      None, None, None, tile, cap_tiles, tiles,
+                                                      n_tiles)
+    return count, idx, tiles, n_tiles
+
+
+def _keepset_build(m, pos, prompt_len, cap, n_keys, max_runs, count, idx, n_runs, runs,
+                   tile, cap_tiles, tiles, n_tiles):
     _need_cuda("keepset_build", pos, prompt_len)
     n_q = pos.numel()
     dev = pos.device
@@ -69,14 +93,27 @@ def keepset_build(m: DaMask, pos: torch.Tensor, prompt_len: torch.Tensor, cap: i
             n_runs = torch.empty(n_q, dtype=torch.int32, device=dev)
         if runs is None:
             runs = torch.empty((n_q, max_runs, 2), dtype=torch.int32, device=dev)
-    for t in (pos, prompt_len, count, idx, n_runs, runs):
+    for t in (pos, prompt_len, count, idx, n_runs, runs, tiles):
         if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
             raise ValueError("keepset_build: int32 contiguous tensors expected")
+    if pos.numel() != n_q or prompt_len.numel() != n_q or count.numel() < n_q or \
+            idx.numel() < n_q * cap:
+        raise ValueError("keepset_build: pos, prompt_len, count [n_q] and idx [n_q, cap] expected")
+    if tile > 0:
+        if tiles is None:
+            tiles = torch.empty((max(cap_tiles, 0), 2), dtype=torch.int32, device=dev)
+        if n_tiles is None:
+            n_tiles = torch.empty(1, dtype=torch.int64, device=dev)
+        if tiles.numel() < 2 * cap_tiles or n_tiles.dtype != torch.int64 or n_tiles.numel() < 1:
+            raise ValueError("keepset_build: tiles int32 [cap_tiles, 2], n_tiles int64 [1] expected")
+    else:
+        tiles = n_tiles = None
     check(load().da_keepset_build(m, n_q, _ptr(pos), _ptr(prompt_len), n_keys, cap,
                                   _ptr(count), _ptr(idx), max_runs, _ptr(n_runs), _ptr(runs),
+                                  int(tile), _ptr(tiles), int(cap_tiles), _ptr(n_tiles),
                                   _stream(pos)),
           "da_keepset_build")
-    return count, idx, n_runs, runs
+    return count, idx, n_runs, runs, tiles, n_tiles
 
 
 def kv_cache(k: torch.Tensor, v: torch.Tensor,
@@ -138,8 +175,11 @@ def sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
         raise ValueError("q and the caches must share dtype fp32 or bf16")
     n_q, hq, hd = q.shape
     hkv = k_cache.shape[1]
-    if idx.dim() != 2 or idx.shape[0] != n_q or not idx.is_contiguous():
-        raise ValueError("idx must be a contiguous [n_q, cap] tensor")
+    if idx.dim() != 2 or idx.shape[0] != n_q or not idx.is_contiguous() or idx.dtype != torch.int32:
+        raise ValueError("idx must be a contiguous int32 [n_q, cap] tensor")
+    for t in (seq, count):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != n_q:
+            raise ValueError("seq and count must be contiguous int32 [n_q] tensors")
     cap = idx.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(hd)
@@ -172,10 +212,17 @@ def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
     given count/idx) the lists keepset_build would write are written too.
     k_new/v_new [n_q, hkv, hd]: the new token's K/V rows, appended to the
     cache at pos before attention (one query per request).  head_wb
-    [hkv, 2] int32 on the device: a (W, B) per kv head.
+    [hq, 2] int32 on the device: a (W, B) per query head.
     Returns (out, lse or None, count or None, idx or None)."""
+    return _decode_masked(m, q, k_cache, v_cache, seq, pos, prompt_len, cap, split, block_table,
+                          scale, out, lse, want_lse, workspace, count, idx, want_lists, k_new,
+                          v_new, head_wb)
+
+
+def _decode_masked(m, q, k_cache, v_cache, seq, pos, prompt_len, cap, split, block_table, scale,
+                   out, lse, want_lse, workspace, count, idx, want_lists, k_new, v_new, head_wb):
     _need_cuda("sparse_decode_attn_masked", q, k_cache, v_cache, seq, pos, prompt_len, block_table,
-               k_new, v_new, head_wb)
+               k_new, v_new, head_wb, out, lse, count, idx)
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be a contiguous [n_q, hq, hd] tensor")
     if q.dtype not in _DTYPE or q.dtype != k_cache.dtype:
@@ -202,16 +249,21 @@ def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
     if (k_new is None) != (v_new is None):
         raise ValueError("k_new and v_new go together")
     if head_wb is not None and (head_wb.dtype != torch.int32 or not head_wb.is_contiguous() or
-                                tuple(head_wb.shape) != (hkv, 2)):
-        raise ValueError("head_wb must be a contiguous int32 [hkv, 2] tensor")
+                                tuple(head_wb.shape) != (hq, 2)):
+        raise ValueError("head_wb must be a contiguous int32 [hq, 2] tensor")
     for t in (k_new, v_new):
         if t is not None and (t.dtype != q.dtype or not t.is_contiguous() or
                               tuple(t.shape) != (n_q, hkv, hd)):
             raise ValueError("k_new and v_new must be contiguous [n_q, hkv, hd] tensors of q's dtype")
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor of q's shape and dtype")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous() or
+                            tuple(lse.shape) != (n_q, hq)):
+        raise ValueError("lse must be a contiguous fp32 [n_q, hq] tensor")
+    kv = kv_cache(k_cache, v_cache, block_table)
     if workspace is None:
         workspace = decode_workspace(n_q, hq, hd, cap, split, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    kv = kv_cache(k_cache, v_cache, block_table)
     check(load().da_sparse_decode_attn_masked(m, _ptr(q), _DTYPE[q.dtype], n_q, hq, hkv, hd,
                                               float(scale), kv, _ptr(seq), _ptr(pos),
                                               _ptr(prompt_len), _ptr(head_wb), _ptr(k_new), _ptr(v_new),
@@ -294,8 +346,6 @@ def band_prefill_attn(m: DaMask, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
         raise ValueError("prompt_len must be int32 [batch]")
     if tiles is None:
         tiles = prefill_tiles_build(m, prompt_len, n)
-    elif tiles.numel() * tiles.element_size() < load().da_prefill_tiles_bytes(bsz, n):
-        raise ValueError("tiles buffer too small for these sizes")
     if scale is None:
         scale = 1.0 / math.sqrt(hd)
     if out is None:
@@ -308,6 +358,7 @@ def band_prefill_attn(m: DaMask, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     st = (ctypes_i64 * 12)(*[t.stride(d) for t in (q, k, v, out) for d in (0, 1, 2)])
     check(load().da_band_prefill_attn(m, 1, bsz, heads, k.shape[1], n, hd, _ptr(q), _ptr(k),
                                       _ptr(v), _ptr(out), st, _ptr(prompt_len), _ptr(tiles),
-                                      float(scale), _ptr(lse), _stream(q)),
+                                      tiles.numel() * tiles.element_size(), float(scale), _ptr(lse),
+                                      _stream(q)),
           "da_band_prefill_attn")
     return out, lse

@@ -41,9 +41,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libdiagattn)")
 
 
+# Per-source additions.  decode.hip: matrix-core accumulators in ordinary
+# VGPRs (the decode kernel rescales them with vector instructions; held in
+# AGPRs they were copied back and forth every block and took a wave a SIMD).
+EXTRA_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

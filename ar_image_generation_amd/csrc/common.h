@@ -30,10 +30,12 @@ inline int ilog2(int64_t x) {
 // d = i - j for a key j >= P inside the window range.  Future keys (d < 0,
 // matrix form only) are kept within B; past keys within B of the main
 // diagonal (BAND) or of any raster-row diagonal k*G (ROWDIAG).
-__host__ __device__ inline bool window_keep(int mode, int d, int B, int G) {
-  if (d < 0) return -d <= B;
+// d is 64-bit so that d = i - j stays exact for any int32 i, j; a past
+// key's d (0 <= d <= i) fits 32 bits, so the residue is a 32-bit modulo.
+__host__ __device__ inline bool window_keep(int mode, int64_t d, int B, int G) {
+  if (d < 0) return -d <= (int64_t)B;
   if (mode == DA_MODE_BAND) return d <= B;
-  const int r = d % G;
+  const int r = (int)((uint32_t)d % (uint32_t)G);
   return r <= B || G - r <= B;
 }
 
@@ -68,6 +70,41 @@ __device__ inline void unpack(const u32x4 w, float (&x)[EPL]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
   }
+}
+
+// Matrix-core operand and result types.
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Max across the lanes l, l ^ 16, l ^ 32 and l ^ 48 (VALU lane swaps): the
+// four lanes that hold one column of a 16x16 matrix-core result.
+__device__ inline float max_over_row_groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum across the lanes l, l ^ 16, l ^ 32 and l ^ 48.
+__device__ inline float sum_over_row_groups(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// LDS position of 16-byte chunk p of row r is p ^ swz(r) in row-major tiles
+// of CPR chunks a row.  With 16 chunks (head_dim 128), under a model of 64
+// four-byte banks, swz spreads both read patterns over all banks: rows read
+// one chunk each (16 consecutive rows, one chunk: swz is a permutation of
+// 0..15) and the transposing reads (8 consecutive rows, two adjacent chunks
+// 2m, 2m+1: swz takes distinct values >> 1 on each aligned 8 rows and keeps
+// bit 0 fixed).  With 8 chunks (head_dim 64) it is r % 8.
+template <int CPR>
+__device__ inline int swz(int r) {
+  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  else return r % CPR;
 }
 
 // DPP lane moves within 16-lane rows.

@@ -120,8 +120,10 @@ struct Tile {
   static constexpr int ROWS = NP * RPP;
   u32x4 k[NP], v[NP];
 
-  // Issues the K and V loads of tile t (no waits).  Slots past the chunk
-  // read position 0's row (always valid, and shared, so it costs cache hits).
+  // Issues the K and V loads of tile t (no waits), nontemporal: each kept
+  // byte is read once (measured 6-8 % faster than cached loads).  Slots past
+  // the chunk read position 0's row (always valid, and shared, so it costs
+  // cache hits).
   __device__ inline void load(const char* kb, const char* vb, const int64_t* off, int64_t off0,
                               int t, int rsub, int nrows) {
     int64_t o[NP];
@@ -135,8 +137,8 @@ struct Tile {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      k[p] = *reinterpret_cast<const u32x4*>(kb + o[p] * ES);
-      v[p] = *reinterpret_cast<const u32x4*>(vb + o[p] * ES);
+      k[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + o[p] * ES));
+      v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + o[p] * ES));
     }
   }
 };
@@ -545,8 +547,8 @@ __global__ void __launch_bounds__(256) decode_kernel(const int32_t* m0_p, const 
       }
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        b.k[p] = *reinterpret_cast<const u32x4*>(kb + o[p] * ES);
-        b.v[p] = *reinterpret_cast<const u32x4*>(vb + o[p] * ES);
+        b.k[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + o[p] * ES));
+        b.v[p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + o[p] * ES));
       }
     } else {
       b.load(kb, vb, rowoff, off0, tt, rsub, nrows);
@@ -665,6 +667,413 @@ __global__ void __launch_bounds__(256) decode_kernel(const int32_t* m0_p, const 
   }
 }
 
+// Matrix-core form of decode_kernel for bf16 caches whose kv heads serve
+// a group of GRP >= 2 query heads.  The group's queries against the kept
+// rows are a small dense contraction: scores S^T = K Q^T (16 rows x 16
+// columns, the GRP query heads in the first columns) and O^T += V^T P^T,
+// on v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x16_bf16.  The matrix
+// cores then do the dot products and the P.V sums that would otherwise be
+// most of the vector work per kept byte (measured: the vector form's
+// arithmetic, not its loads, set its speed on the GQA workloads).
+//
+// Layout.  Each wave takes blocks of 16 kept rows (wave w: blocks w, w+4,
+// ...).  Lane l loads, for row l % 16 of the block, the 64 bytes of K and of
+// V at dims 32c + 8 (l / 16) .. + 8, c = 0 .. HD/32 - 1: that is the A
+// operand of S^T = K Q^T as loaded, so K goes straight from its load into
+// the matrix core.  The result gives lane l the scores of rows 4 (l/16) + r,
+// r = 0..3, for query head l % 16 -- the layout of the B operand P^T of the
+// second product, so the softmax runs in place.  V goes through a 4 KiB LDS
+// staging area of the wave and comes back transposed (ds_read_b64_tr_b16)
+// as the A operand V^T.  Two blocks are in flight per wave (K and V in
+// registers); loads are nontemporal (each byte is read once).  The online
+// softmax keeps a reference max per query head that moves only when the
+// block max passes it by more than 2^8 (log2 domain), so the output
+// accumulators are rescaled rarely.  Rows (element offsets, and positions
+// for per-head masks) come from an LDS table filled at the start, the same
+// entries in the same order as decode_kernel reads.  The four waves' states
+// meet in LDS at the end, as in decode_kernel, whose output and partial
+// formats are kept (the merge kernel serves both).
+template <int HD, int GRP, int FORM>
+__global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, const int32_t* m1_p,
+                                                          const int32_t* seq_p, int hkv_p,
+                                                          int max_split_p, int cap_p, int split_p,
+                                                          const void* k_p, const void* v_p,
+                                                          const void* q_p, DecodeArgs a) {
+  static_assert(GRP >= 2 && GRP <= 16, "query heads of a group are matrix-core columns");
+  constexpr bool MASKED = FORM >= 1;
+  constexpr bool PERHEAD = FORM == 2;
+  constexpr int NC = HD / 32;         // 32-dim contraction steps of S^T = K Q^T
+  constexpr int NB = HD / 16;         // 16-dim output blocks of O^T
+  constexpr int CPR = HD / 8;         // 16-byte chunks per row
+  constexpr int LPR = CPR;            // output combine: threads per head (8 elements each)
+
+  extern __shared__ int64_t rowoff[];                 // [split] element offsets (+ positions)
+  __shared__ float red_m[4][GRP];
+  __shared__ float red_l[4][GRP];
+  // per-wave V staging during the loop; the waves' outputs afterwards
+  constexpr int VST = 16 * HD;                        // bf16 elements per wave
+  constexpr int RED = GRP * HD * 2;                   // fp32 outputs per wave, in bf16 units
+  __shared__ __attribute__((aligned(16))) uint16_t stage[4 * (VST > RED ? VST : RED)];
+  __shared__ u32x4 newrow[2 * CPR];                   // KV append: the new K, V rows
+
+  const int t = threadIdx.x;
+  const int wave = t >> 6;
+  const int lane = t & 63;
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+
+  const int bid = blockIdx.x;
+  const int s = bid % max_split_p;
+  const int qg = bid / max_split_p;
+  const int qi = qg / hkv_p;
+  const int g = qg % hkv_p;
+  int i_m = 0, P_m = 0, sq_m = 0, cnt_l = 0;
+  if constexpr (MASKED) {
+    i_m = m0_p[qi];
+    P_m = m1_p[qi];
+    sq_m = seq_p[qi];
+  } else {
+    cnt_l = m0_p[qi];
+    sq_m = seq_p[qi];
+  }
+  const int r0 = s * split_p;
+  const int lim = cap_p - r0 < split_p ? cap_p - r0 : split_p;   // >= 1
+
+  // ---- stage 0: the group's query rows into LDS as 16 rows (rows past the
+  // group zero), chunks swizzled like the V staging; lane l reads its B
+  // operand Q^T (query head l % 16) from there for each block
+  __shared__ __attribute__((aligned(16))) uint16_t qsh[16 * HD];
+  for (int e = t; e < 16 * CPR; e += 256) {
+    const int h = e / CPR, ch = e % CPR;
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (h < GRP)
+      w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(q_p) +
+                                          (((int64_t)qi * hkv_p + g) * GRP + h) * HD + ch * 8);
+    *reinterpret_cast<u32x4*>(qsh + h * HD + ((ch ^ swz<CPR>(h)) * 8)) = w;
+  }
+  // per-head masks: this lane's head's window and band, and the group's
+  // widest, whose keep-set contains every head's
+  int Wh = a.W, Bh = a.B, Wg = a.W, Bg = a.B;
+  if constexpr (PERHEAD) {
+    const int32_t* wb = a.head_wb + 2 * (int64_t)g * GRP;
+    Wg = 0;
+    Bg = 0;
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      const int w = wb[2 * h] > 0 ? wb[2 * h] : 0, b = wb[2 * h + 1] > 0 ? wb[2 * h + 1] : 0;
+      Wg = w > Wg ? w : Wg;
+      Bg = b > Bg ? b : Bg;
+      if (h == lr) {
+        Wh = w;
+        Bh = b;
+      }
+    }
+  }
+  const char* kb = reinterpret_cast<const char*>(k_p) + ((int64_t)g * a.head_stride + 8 * lg) * 2;
+  const char* vb = reinterpret_cast<const char*>(v_p) + ((int64_t)g * a.head_stride + 8 * lg) * 2;
+
+  int cnt, nrows;
+  const int sq = clampi(sq_m, 0, a.n_seq - 1);
+  const int32_t* bt = a.block_table ? a.block_table + (int64_t)sq * a.bt_stride : nullptr;
+  KeepCF kc{};
+  int n_keep = 0, sub_row = -1;
+  bool appending = false, stores = false;
+  u32x4 nkv = u32x4{0u, 0u, 0u, 0u};
+  auto store_new_row = [&]() {
+    if (t < 2 * CPR) {
+      const int64_t o = row_offset(a, bt, sq, i_m);
+      char* base = reinterpret_cast<char*>(const_cast<void*>(t < CPR ? a.k : a.v));
+      *reinterpret_cast<u32x4*>(base + ((int64_t)g * a.head_stride + (t % CPR) * 8 + o) * 2) = nkv;
+    }
+  };
+  if constexpr (MASKED) {
+    appending = a.k_new != nullptr;
+    if (appending && t < 2 * CPR) {
+      const void* src = t < CPR ? a.k_new : a.v_new;
+      const int64_t off = ((int64_t)qi * a.hkv + g) * HD + (t % CPR) * 8;
+      nkv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(src) + off);
+    }
+    const bool bad = i_m < 0 || P_m < 0;
+    stores = appending && !bad && i_m < a.max_len;
+    kc = keep_cf(a.mode, i_m, P_m, Wg, Bg, a.G, bad);
+    n_keep = kc.size();
+    cnt = n_keep < a.cap ? n_keep : a.cap;
+    if (stores && n_keep <= a.cap && n_keep - 1 >= r0 && n_keep - 1 < r0 + lim) sub_row = n_keep - 1 - r0;
+    if (r0 >= cnt) {
+      if (a.count_out != nullptr && g == 0 && s == 0 && t == 0) a.count_out[qi] = n_keep;
+      if (a.ws_cnt && s == 0 && t == 0) a.ws_cnt[(int64_t)qi * a.hkv + g] = n_keep;
+      if (stores && a.max_split == 1) store_new_row();
+      return;
+    }
+  } else {
+    cnt = cnt_l < a.cap ? cnt_l : a.cap;
+    if (r0 >= cnt) return;
+  }
+  nrows = cnt - r0 < a.split ? cnt - r0 : a.split;
+
+  // ---- stage 1: element offset (and, per-head masks, position) of every
+  // row of the chunk into LDS, one round trip for the list entries or
+  // block-table entries; with them, before any K/V load is issued, every
+  // store the step owes besides its output: the lists (kv-head-0
+  // workgroups write the entries of their chunk), the keep-set size for the
+  // merge, and the appended row (in the cache and, for this workgroup's own
+  // use, in LDS).  No store or conditional load then sits among the K/V
+  // loads, so the compiler's wait counts for them stay exact.
+  __shared__ int64_t app_off;
+  const bool lists_out = MASKED && a.count_out != nullptr && g == 0;
+  int32_t* my_out = lists_out ? a.idx_out + (int64_t)qi * a.cap + r0 : nullptr;
+  if constexpr (MASKED) {
+    if (stores && t == 0) app_off = row_offset(a, bt, sq, i_m);
+    if (lists_out && s == 0 && t == 0) a.count_out[qi] = n_keep;
+    if (a.ws_cnt && s == 0 && t == 0) a.ws_cnt[(int64_t)qi * a.hkv + g] = n_keep;
+    if (appending && t < 2 * CPR) newrow[t] = nkv;
+  }
+  // (positions follow the offsets: the table holds min(split, cap) rows)
+  int32_t* rowpos = reinterpret_cast<int32_t*>(rowoff + (split_p < cap_p ? split_p : cap_p));
+  {
+    constexpr int IPT = 4;
+    const int32_t* myidx = MASKED ? nullptr : m1_p + (int64_t)qi * cap_p + r0;
+    for (int base = 0; base < nrows; base += IPT * 256) {
+      int jj[IPT];
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) {
+        const int r = base + u * 256 + t;
+        const int rc = r < nrows ? r : nrows - 1;
+        int j;
+        if constexpr (MASKED) j = kc.entry(r0 + rc);
+        else j = myidx[rc];
+        jj[u] = clampi(j, 0, a.max_len - 1);
+        if constexpr (PERHEAD) {
+          if (r < nrows) rowpos[r] = j;
+        }
+        if (lists_out && r < nrows) my_out[r] = j;
+      }
+      int64_t o[IPT];
+      if (bt) {
+        int pg[IPT];
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) pg[u] = bt[jj[u] >> a.ps_shift];
+#pragma unroll
+        for (int u = 0; u < IPT; ++u)
+          o[u] = (int64_t)clampi(pg[u], 0, a.n_pages - 1) * a.page_stride +
+                 (int64_t)(jj[u] & a.ps_mask) * a.slot_stride;
+      } else {
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) o[u] = (int64_t)sq * a.page_stride + (int64_t)jj[u] * a.slot_stride;
+      }
+#pragma unroll
+      for (int u = 0; u < IPT; ++u) {
+        const int r = base + u * 256 + t;
+        if (r < nrows) rowoff[r] = o[u];
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (MASKED) {
+    // KV append: one chunk -- this one -- or, with several, the chunk that
+    // attends the last entry (position i itself when the list is not cut)
+    if (stores && (a.max_split == 1 || (cnt - 1) / a.split == s) && t < 2 * CPR) {
+      char* base = reinterpret_cast<char*>(const_cast<void*>(t < CPR ? a.k : a.v));
+      *reinterpret_cast<u32x4*>(base + ((int64_t)g * a.head_stride + (t % CPR) * 8 + app_off) * 2) = nkv;
+    }
+  }
+
+  // B operand chunk c of S^T = K Q^T: query head l % 16, dims 32c + 8 (l / 16)
+  auto qop = [&](int c, int zo) {
+    return *reinterpret_cast<const bf16x8*>(qsh + zo + lr * HD + (((4 * c + lg) ^ swz<CPR>(lr)) * 8));
+  };
+  // KV append: scores of the new K row for this lane's query head, on the
+  // matrix core with the same operand layout as every block's rows
+  float s_new = 0.f;
+  if constexpr (MASKED) {
+    if (sub_row >= 0) {
+      f32x4 sn = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        sn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, newrow[4 * c + lg]), qop(c, 0),
+                                                     sn, 0, 0, 0);
+      s_new = sn[0];
+    }
+  }
+
+  const int nblk = (nrows + 15) / 16;
+  uint16_t* vst = stage + wave * (VST > RED ? VST : RED);
+
+  // ---- stage 2: blocks of 16 rows, two in flight per wave
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // One K and one V buffer: the next block's K is issued as soon as this
+  // block's scores are out, its V once this block's V is staged, so every
+  // wave has a block of loads in flight while it computes; sixteen waves a
+  // CU then hold 128 KiB of reads in flight
+  u32x4 kk[NC], vv[NC];
+  auto byte_off = [&](int blk) {
+    const int row = blk * 16 + lr;
+    return rowoff[row < nrows ? row : nrows - 1] * 2;
+  };
+  auto load_k = [&](int blk) {
+    const int64_t off = byte_off(blk);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      kk[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + off + 64 * c));
+  };
+  auto load_v = [&](int blk) {
+    const int64_t off = byte_off(blk);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      vv[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + off + 64 * c));
+  };
+  auto process = [&](int blk) {
+    // LDS addresses (query operand, V staging, transposing reads) are taken
+    // from an offset the compiler cannot see as loop-invariant, so they are
+    // recomputed per block instead of being held in registers through the
+    // loop (which spilled)
+    int zo = 0;
+    __asm__ volatile("" : "+v"(zo));
+    uint16_t* const vsw = vst + zo;
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[c]), qop(c, zo), sc, 0, 0, 0);
+    // the refill of this K buffer stays behind the products that read it:
+    // the empty asm takes their result and orders memory, so the scheduler
+    // can neither hoist the loads above the products (which would copy the
+    // buffer and wait for every load in flight) nor sink the products
+    __asm__ volatile("" : "+v"(sc)::"memory");
+    load_k(blk + 4);
+    // V to the wave's staging area, row-major with swizzled chunks
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      *reinterpret_cast<u32x4*>(vsw + lr * HD + (((4 * c + lg) ^ swz<CPR>(lr)) * 8)) = vv[c];
+    if constexpr (MASKED) {
+      // KV append: the new token's row is row sub_row % 16 of its block.
+      // Its V row goes over the staged one, and its scores are the ones
+      // computed from its K row at the start (the same products on the same
+      // matrix core, so the same values).  The block test is uniform.
+      if (sub_row >= 0 && (sub_row >> 4) == blk) {
+        const int rr = sub_row & 15;
+        if (lr == rr) {
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+            *reinterpret_cast<u32x4*>(vsw + lr * HD + (((4 * c + lg) ^ swz<CPR>(lr)) * 8)) =
+                newrow[CPR + 4 * c + lg];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = (lg == (rr >> 2) && r == (rr & 3)) ? s_new : sc[r];
+      }
+    }
+    // likewise the refill of the V buffer stays behind its staging stores
+    __asm__ volatile("" ::: "memory");
+    load_v(blk + 4);
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = blk * 16 + 4 * lg + r;
+      bool keep = row < nrows;
+      if constexpr (PERHEAD) {
+        const int j = rowpos[row < nrows ? row : 0];
+        const int64_t d = (int64_t)i_m - j;
+        keep = keep && (a.mode == DA_MODE_DENSE || j < P_m || (d <= Wh && window_keep(a.mode, d, Bh, a.G)));
+      }
+      sv[r] = keep ? sc[r] * a.qscale : -INFINITY;
+    }
+    const float mt = max_over_row_groups(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    if (__any(mt > m + 8.f)) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[nb][r] *= alpha;
+      m = mn;
+    }
+    const float mref = m == -INFINITY ? 0.f : m;
+    v4i16 pb;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = __builtin_amdgcn_exp2f(sv[r] - mref);
+      lsum += p;
+      pb[r] = __builtin_bit_cast(short, (__bf16)p);
+    }
+    // O^T += V^T P^T, one 16-dim block at a time
+    const int vr = 4 * lg + (lr >> 2);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint16_t* pv = vsw + vr * HD + (((2 * nb + ((lr & 3) >> 1)) ^ swz<CPR>(vr)) * 8) + (lr & 1) * 4;
+      const v4i16 av = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(pv));
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, o[nb], 0, 0, 0);
+    }
+  };
+  // Every load is issued unconditionally (blocks past the chunk read its
+  // last row again: cache hits), so the compiler's wait counts never merge
+  // paths with different numbers of loads in flight.
+  if (wave < nblk) {
+    load_k(wave);
+    load_v(wave);
+    for (int blk = wave; blk < nblk; blk += 4) process(blk);
+  }
+
+  // ---- combine: per query head the wave's max, sum and output, then the
+  // four waves (LDS), then the output or the chunk's partial
+  lsum = sum_over_row_groups(lsum);
+  __syncthreads();                      // every wave done with its V staging
+  float* redo = reinterpret_cast<float*>(stage) + wave * (GRP * HD);
+  if (lr < GRP) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) redo[lr * HD + 16 * nb + 4 * lg + r] = o[nb][r];
+    if (lg == 0) {
+      red_m[wave][lr] = m;
+      red_l[wave][lr] = lsum;
+    }
+  }
+  __syncthreads();
+  if (t < GRP * LPR) {
+    const int h = t / LPR;
+    const int cc = t % LPR;
+    const float* ro = reinterpret_cast<const float*>(stage);
+    float M = fmaxf(fmaxf(red_m[0][h], red_m[1][h]), fmaxf(red_m[2][h], red_m[3][h]));
+    const float Mr = M == -INFINITY ? 0.f : M;
+    float fw[4];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      fw[w] = exp2f(red_m[w][h] - Mr);
+      L = fmaf(fw[w], red_l[w][h], L);
+    }
+    float ov[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x = fmaf(fw[w], ro[(w * GRP + h) * HD + cc * 8 + e], x);
+      ov[e] = x;
+    }
+    const int64_t row = (int64_t)qi * a.hq + g * GRP + h;
+    if (cnt <= a.split) {
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ov[e] *= inv;
+      store_out<true, 8>(a.out, row * HD + cc * 8, ov);
+      if (a.lse && cc == 0) a.lse[row] = (M + log2f(L)) * kLn2;
+    } else {
+      float* dst = a.ws_o + (row * a.max_split + s) * HD + cc * 8;
+#pragma unroll
+      for (int e = 0; e < 8; e += 4)
+        *reinterpret_cast<float4*>(dst + e) = make_float4(ov[e], ov[e + 1], ov[e + 2], ov[e + 3]);
+      if (cc == 0) {
+        a.ws_ml[(row * a.max_split + s) * 2] = M;
+        a.ws_ml[(row * a.max_split + s) * 2 + 1] = L;
+      }
+    }
+  }
+}
+
 // Log-sum-exp merge of the chunk partials of one (query, head): one wave.
 // Lanes first read the chunks' (max, sum) pairs in parallel, then every lane
 // accumulates its HD/64 output elements over the chunks.
@@ -731,6 +1140,18 @@ static decode_fn pick_grp(int grp, int np) {
     default: return pick_np<BF16, HD, 8, FORM>(np);
   }
 }
+
+// Matrix-core kernel for bf16 groups of 2, 4 or 8 query heads a kv head.
+template <int FORM>
+static decode_fn pick_mfma(int head_dim, int grp) {
+  if (head_dim == 64)
+    return grp == 2 ? decode_mfma_kernel<64, 2, FORM>
+                    : grp == 4 ? decode_mfma_kernel<64, 4, FORM> : decode_mfma_kernel<64, 8, FORM>;
+  return grp == 2 ? decode_mfma_kernel<128, 2, FORM>
+                  : grp == 4 ? decode_mfma_kernel<128, 4, FORM> : decode_mfma_kernel<128, 8, FORM>;
+}
+
+static bool use_mfma(da_dtype dtype, int grp) { return dtype == DA_BF16 && grp >= 2; }
 
 template <int FORM>
 static decode_fn pick_kernel(da_dtype dtype, int head_dim, int grp, int np) {
@@ -884,12 +1305,21 @@ static int launch_decode(const DecodeArgs& a, da_dtype dtype, int head_dim, void
   const int esz = dtype == DA_BF16 ? 2 : 4;
   const int chunk = a.split < a.cap ? a.split : a.cap;
   const int64_t blocks = int64_t(a.n_q) * a.hkv * a.max_split;
-  // row offsets in LDS: every list, and the mask form of a paged cache
-  const size_t lds = FORM >= 1 && !a.block_table ? 0 : (size_t)chunk * sizeof(int64_t);
-  const int np = tile_depth(chunk, 256 / (head_dim * esz / 16), blocks, lds, [&](int d) {
-    return pick_kernel<FORM>(dtype, head_dim, a.hq / a.hkv, d);
-  });
-  const decode_fn dk = pick_kernel<FORM>(dtype, head_dim, a.hq / a.hkv, np);
+  const int grp = a.hq / a.hkv;
+  decode_fn dk;
+  size_t lds;
+  if (use_mfma(dtype, grp)) {
+    // row table in LDS: offsets, and positions for per-head masks
+    lds = (size_t)chunk * (sizeof(int64_t) + (FORM == 2 ? sizeof(int32_t) : 0));
+    dk = pick_mfma<FORM>(head_dim, grp);
+  } else {
+    // row offsets in LDS: every list, and the mask form of a paged cache
+    lds = FORM >= 1 && !a.block_table ? 0 : (size_t)chunk * sizeof(int64_t);
+    const int np = tile_depth(chunk, 256 / (head_dim * esz / 16), blocks, lds, [&](int d) {
+      return pick_kernel<FORM>(dtype, head_dim, grp, d);
+    });
+    dk = pick_kernel<FORM>(dtype, head_dim, grp, np);
+  }
   const merge_fn mk = dtype == DA_BF16 ? (head_dim == 64 ? merge_kernel<true, 64> : merge_kernel<true, 128>)
                                        : (head_dim == 64 ? merge_kernel<false, 64> : merge_kernel<false, 128>);
   const int32_t* m0 = FORM >= 1 ? a.pos : a.count;
@@ -957,6 +1387,8 @@ extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_
     return fail(DA_EINVAL, "k_new and v_new must both be given or both be NULL");
   if (head_wb && count)
     return fail(DA_EINVAL, "per-head masks give per-head keep-sets: no per-query lists");
+  if (head_wb && !use_mfma(dtype, hq / (hkv > 0 ? hkv : 1)) && hq != hkv)
+    return fail(DA_ENOTSUP, "per-query-head masks with groups of query heads need bf16");
   if (((uintptr_t)k_new | (uintptr_t)v_new) % 16) return fail(DA_EINVAL, "k_new and v_new must be 16-byte aligned");
   clear_error();
   if (n_q == 0) return DA_OK;
@@ -976,3 +1408,4 @@ extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_
   return head_wb ? launch_decode<2>(a, dtype, head_dim, stream)
                  : launch_decode<1>(a, dtype, head_dim, stream);
 }
+

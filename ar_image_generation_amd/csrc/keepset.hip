@@ -42,23 +42,24 @@ __global__ void __launch_bounds__(256) keepset_kernel(const int32_t* pos, const 
     }
     return;
   }
-  const int L = a.causal ? i + 1 : a.n_keys;
+  // positions and window ends in 64 bits: i + 1 and i + B may pass INT32_MAX
+  const int64_t L = a.causal ? (int64_t)i + 1 : (int64_t)a.n_keys;
   int32_t* my_idx = a.idx + (int64_t)q * a.cap;
   int32_t* my_runs = a.runs ? a.runs + (int64_t)q * a.max_runs * 2 : nullptr;
 
-  int Pc, wlo, whi;
+  int64_t Pc, wlo, whi;
   if (a.mode == DA_MODE_DENSE) {
     Pc = L;           // everything up to L is one run
     wlo = 1;
     whi = 0;          // empty window
   } else {
-    Pc = P < L ? P : L;
-    wlo = i - a.W > Pc ? i - a.W : Pc;
-    whi = a.causal ? i : (L - 1 < i + a.B ? L - 1 : i + a.B);
+    Pc = P < L ? (int64_t)P : L;
+    wlo = (int64_t)i - a.W > Pc ? (int64_t)i - a.W : Pc;
+    whi = a.causal ? (int64_t)i : (L - 1 < (int64_t)i + a.B ? L - 1 : (int64_t)i + a.B);
   }
 
-  const int pw = Pc < a.cap ? Pc : a.cap;
-  for (int r = lane; r < pw; r += 64) my_idx[r] = r;
+  const int64_t pw = Pc < a.cap ? Pc : (int64_t)a.cap;
+  for (int64_t r = lane; r < pw; r += 64) my_idx[r] = (int32_t)r;
 
   // The prompt run is run 0 unless the first window position continues it.
   const bool joins = Pc > 0 && wlo == Pc && wlo <= whi &&
@@ -67,20 +68,20 @@ __global__ void __launch_bounds__(256) keepset_kernel(const int32_t* pos, const 
   if (Pc > 0 && !joins) {
     if (lane == 0 && my_runs && a.max_runs > 0) {
       my_runs[0] = 0;
-      my_runs[1] = Pc;
+      my_runs[1] = (int32_t)Pc;
     }
     nr = 1;
   }
 
-  int n = Pc;
+  int64_t n = Pc;
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int base = wlo; base <= whi; base += 64) {
-    const int j = base + lane;
+  for (int64_t base = wlo; base <= whi; base += 64) {
+    const int64_t j = base + lane;
     const bool kp = j <= whi && window_keep(a.mode, i - j, a.B, a.G);
     const uint64_t kb = __ballot(kp);
     if (kp) {
-      const int slot = n + __popcll(kb & below);
-      if (slot < a.cap) my_idx[slot] = j;
+      const int64_t slot = n + __popcll(kb & below);
+      if (slot < a.cap) my_idx[slot] = (int32_t)j;
     }
     n += __popcll(kb);
 
@@ -89,20 +90,70 @@ __global__ void __launch_bounds__(256) keepset_kernel(const int32_t* pos, const 
     const uint64_t eb = __ballot(end);
     if (end && my_runs) {
       const int k = nr + __popcll(eb & below);
-      int s = j;
+      int64_t s = j;
       while (s - 1 >= wlo && window_keep(a.mode, i - (s - 1), a.B, a.G)) --s;
       if (s == wlo && joins) s = 0;
       if (k < a.max_runs) {
-        my_runs[2 * k] = s;
-        my_runs[2 * k + 1] = j - s + 1;
+        my_runs[2 * k] = (int32_t)s;
+        my_runs[2 * k + 1] = (int32_t)(j - s + 1);
       }
     }
     nr += __popcll(eb);
   }
   if (lane == 0) {
-    a.count[q] = n;
+    a.count[q] = (int32_t)(n < INT32_MAX ? n : INT32_MAX);   // 2^31 keys: saturated
     if (a.n_runs) a.n_runs[q] = nr;
   }
+}
+
+
+// Tile list of the keep-sets: each query's first min(count, cap) entries
+// cut into consecutive chunks of `tile` entries, in query order, as
+// (query, first entry) pairs -- the split-KV work list.  One workgroup:
+// queries are taken 1024 at a time, each thread counts its query's chunks,
+// a workgroup-wide exclusive scan gives each query its first list slot,
+// and the running total carries over to the next 1024 queries.  Entries
+// past cap_tiles are not written; n_tiles receives the true total.
+__global__ void __launch_bounds__(1024) keepset_tiles_kernel(const int32_t* count, int n_q, int cap,
+                                                             int tile, int32_t* tiles,
+                                                             int64_t cap_tiles, int64_t* n_tiles) {
+  __shared__ int64_t wsum[16];
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  int64_t total = 0;
+  for (int base = 0; base < n_q; base += 1024) {
+    const int q = base + t;
+    int c = q < n_q ? count[q] : 0;
+    c = c < 0 ? 0 : (c < cap ? c : cap);
+    const int64_t nt = (c + (int64_t)tile - 1) / tile;
+    // inclusive scan within the wave, then across the 16 waves
+    int64_t x = nt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int64_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      before += w < wave ? wsum[w] : 0;
+      all += wsum[w];
+    }
+    const int64_t first = total + before + x - nt;
+    for (int64_t k = 0; k < nt; ++k) {
+      const int64_t e = first + k;
+      if (e < cap_tiles) {
+        tiles[2 * e] = q;
+        tiles[2 * e + 1] = (int32_t)(k * tile);
+      }
+    }
+    total += all;
+    __syncthreads();                   // wsum is rewritten by the next round
+  }
+  if (t == 0) *n_tiles = total;
 }
 
 }  // namespace da
@@ -112,7 +163,8 @@ using namespace da;
 extern "C" int da_keepset_build(const da_mask* m, int32_t n_q, const int32_t* pos,
                                 const int32_t* prompt_len, int32_t n_keys, int32_t cap,
                                 int32_t* count, int32_t* idx, int32_t max_runs,
-                                int32_t* n_runs, int32_t* runs, void* stream) {
+                                int32_t* n_runs, int32_t* runs, int32_t tile, int32_t* tiles,
+                                int64_t cap_tiles, int64_t* n_tiles, void* stream) {
   int rc = check_mask(m);
   if (rc) return rc;
   if (n_q < 0) return fail(DA_EINVAL, "n_q=%d < 0", n_q);
@@ -123,7 +175,17 @@ extern "C" int da_keepset_build(const da_mask* m, int32_t n_q, const int32_t* po
   if ((runs == nullptr) != (n_runs == nullptr))
     return fail(DA_EINVAL, "runs and n_runs must both be given or both be NULL");
   if (runs && max_runs < 1) return fail(DA_EINVAL, "max_runs=%d < 1", max_runs);
+  if ((tiles == nullptr) != (n_tiles == nullptr))
+    return fail(DA_EINVAL, "tiles and n_tiles must both be given or both be NULL");
+  if (n_tiles && (tile < 1 || cap_tiles < 0))
+    return fail(DA_EINVAL, "tile=%d must be >= 1 and cap_tiles=%lld >= 0", tile, (long long)cap_tiles);
   clear_error();
+  if (n_q == 0 && n_tiles) {
+    // an empty tile list still has its size written
+    hipLaunchKernelGGL(keepset_tiles_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, count, 0, cap,
+                       tile, tiles, cap_tiles, n_tiles);
+    return check_launch("keepset_tiles_kernel");
+  }
   if (n_q == 0) return DA_OK;
   KeepsetArgs a;
   a.mode = m->mode;
@@ -143,5 +205,9 @@ extern "C" int da_keepset_build(const da_mask* m, int32_t n_q, const int32_t* po
   a.runs = runs;
   const int blocks = (n_q + 3) / 4;
   hipLaunchKernelGGL(keepset_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, a.pos, a.prompt, a.n_q, a);
-  return check_launch("keepset_kernel");
+  rc = check_launch("keepset_kernel");
+  if (rc || !n_tiles) return rc;
+  hipLaunchKernelGGL(keepset_tiles_kernel, dim3(1), dim3(1024), 0, (hipStream_t)stream, count, n_q, cap,
+                     tile, tiles, cap_tiles, n_tiles);
+  return check_launch("keepset_tiles_kernel");
 }

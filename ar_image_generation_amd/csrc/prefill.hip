@@ -35,8 +35,6 @@
 
 namespace da {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -77,7 +75,7 @@ __device__ inline bool range_has_kept(int ilo, int ihi, int jlo, int jhi, int P,
   const int dhi = ihi - jlo < W ? ihi - jlo : W;
   if (dlo > dhi) return false;
   if (mode == DA_MODE_BAND) return dlo <= B;
-  if (2 * B + 1 >= G) return true;
+  if (2 * (int64_t)B + 1 >= G) return true;
   const int r = dlo % G;
   if (r <= B || r >= G - B) return true;
   return dlo - r + G - B <= dhi;                 // next band start
@@ -131,35 +129,11 @@ __device__ inline void dma16(const void* sbase, uint32_t voff, const void* lds) 
   __asm__ volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(dst) : "memory");
 }
 
-// LDS position of 16-byte chunk p of key row r is p ^ swz(r).  With 16
-// chunks a row (head_dim 128), under a model of 64 four-byte banks, swz
-// spreads both read patterns over all banks: the K reads (16 consecutive
-// rows, one chunk: swz is a permutation of 0..15) and the transposing V
-// reads (8 consecutive rows, two adjacent chunks 2m, 2m+1: swz takes
-// distinct values >> 1 on each aligned 8 rows and keeps bit 0 fixed).  The
-// bank-conflict counter did not drop with it, so that model is not the
-// whole story on this part.  With 8 chunks (head_dim 64) it is r % 8.
-template <int CPR>
-__device__ inline int swz(int r) {
-  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
-  else return r % CPR;
-}
-
-// Max across the lanes l, l ^ 16, l ^ 32 and l ^ 48 (VALU lane swaps).
-__device__ inline float max_over_row_groups(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-// Sum across the lanes l, l ^ 16, l ^ 32 and l ^ 48.
-__device__ inline float sum_over_row_groups(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
+// K and V tiles sit in LDS row-major with 16-byte chunk p of row r at
+// position p ^ swz(r) (common.h): the K reads and the transposing V reads
+// then spread over the banks under a 64-bank model.  The bank-conflict
+// counter did not drop with it, so that model is not the whole story on
+// this part.
 
 // ---------------------------------------------------------------- tile lists
 // For query tile qt of batch b: the key tiles (BN keys) holding a kept pair,
@@ -320,7 +294,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
     // every k with r - kG in [-B, 63 + B]
     for (int r = t; r < G; r += NTHREADS) {
       uint64_t w = 0;
-      if (2 * Bw + 1 >= G) {
+      if (2 * (int64_t)Bw + 1 >= G) {
         w = ~uint64_t(0);
       } else {
         int c0 = r;
@@ -546,8 +520,12 @@ static void fill_common(PrefillArgs& a, const da_mask* m, int32_t batch, int32_t
   a.batch = batch;
   a.n = n;
   a.mode = m->mode;
-  a.W = m->W;
-  a.B = m->B;
+  // Distances between a row and a key of one sequence are below n, so a
+  // window or band of n or more keeps what an unbounded one keeps: W and B
+  // are clamped to n, which keeps every row/key offset computation (x - W,
+  // c + B, ...) far inside the int range and every band loop short.
+  a.W = m->W < n ? m->W : n;
+  a.B = m->B < n ? m->B : n;
   a.G = m->G;
   a.inv_g = 1.f / (float)m->G;
   a.n_qt = n_query_tiles(n);
@@ -583,7 +561,8 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
                                     int32_t kv_heads, int32_t n, int32_t head_dim,
                                     const void* q, const void* k, const void* v, void* out,
                                     const int64_t* strides, const int32_t* prompt_len,
-                                    const void* tiles, float scale, float* lse, void* stream) {
+                                    const void* tiles, int64_t tiles_bytes, float scale, float* lse,
+                                    void* stream) {
   int rc = check_mask(m);
   if (rc) return rc;
   if (!m->causal) return fail(DA_ENOTSUP, "prefill needs a causal mask");
@@ -607,6 +586,10 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
                 (long long)strides[5], (long long)strides[8]);
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)tiles) % 16)
     return fail(DA_EINVAL, "q, k, v, out and tiles must be 16-byte aligned");
+  const int64_t need = da_prefill_tiles_bytes(batch, n);
+  if (tiles_bytes < need)
+    return fail(DA_ECAPACITY, "tiles buffer %lld bytes < %lld for batch %d, n %d", (long long)tiles_bytes,
+                (long long)need, batch, n);
   clear_error();
   if (batch == 0 || n == 0) return DA_OK;
   PrefillArgs a{};

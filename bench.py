@@ -1,17 +1,19 @@
 """Benchmark of the sparse decode hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = keep-set build + sparse decode attention (plus the chunk merge
-when a keep-set spans several chunks) for one batch of the LlamaGen-like
-decode workload: 16 requests x 32 heads, head_dim 128, bf16 KV, prompt 120
-tokens, 32x32 raster grid, W = 3 rows, B = 2, row-diagonal mode -- as one
-launch (sparse_decode_attn_masked, which also writes the keep-set lists).
-The same step as two launches (keepset_build, sparse_decode_attn) is
-reported beside it, with the dense run at the same shape, the other decode
-workloads, a streaming-read probe of the same byte count, a KV append run,
-the ring-cache (KV residency) run, a B x W mask sweep and the band prefill.
-Inputs are seeded synthetic tensors, resident in HBM before timing starts.
+when a keep-set spans several chunks) for one batch of a decode workload, by
+default the largest one: paged KV decode of 128 requests x 32 query / 8 kv
+heads, head_dim 128, bf16, 16-slot pages behind a seeded random block
+table, prompts of 64..300 tokens, a 48x48 raster grid, W = 2 rows, B = 2,
+row-diagonal mode (the band mode is reported beside it) -- as one launch
+(sparse_decode_attn_masked, which also writes the keep-set lists).  The same
+step as two launches (keepset_build, sparse_decode_attn) is reported beside
+it, with the dense run at the same shape, the other decode workloads, a
+streaming-read probe of the same byte count, a KV append run, the ring-cache
+(KV residency) run, a B x W mask sweep and the band prefill.  Inputs are
+seeded synthetic tensors, resident in HBM before timing starts.
 
 Cold-cache timing: the KV cache is replicated on the device and step k reads
 copy k mod n, with n chosen so that at least 1 GiB of other kept rows is
@@ -339,32 +341,55 @@ class PrefillBench:
         return rec
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, budget_s=12.0):
-    """The oracle, as it stands, on the same workload: all queries of the
-    batch, repeated until about `budget_s` seconds of CPU work."""
+    """The oracle, as it stands, on the same workload: queries of the batch
+    taken in order, one at a time, until about `budget_s` seconds of CPU work
+    (the sample).  The oracle is plain per-(query, head) numpy; its BLAS is
+    held to one thread, which is the parallelism it actually has (small
+    matrix-vector products), so `cores` is 1."""
     import numpy as np
     import oracle as O
     import workloads as wl
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+        from threadpoolctl import threadpool_limits
+    except ImportError:
+        threadpool_limits = None
     inp = wl.decode_inputs(cfg)
-    args = (inp.q.double().numpy(), inp.k_logical.double().numpy(), inp.v_logical.double().numpy(),
-            inp.pos.numpy(), inp.prompt_len.numpy(), inp.seq.numpy())
+    # float32 copies hold the bf16 values exactly; the oracle takes each
+    # slice it reads to float64 itself
+    q = inp.q.float().numpy()
+    K = inp.k_logical.float().numpy()
+    V = inp.v_logical.float().numpy()
+    pos, prompt, seq = inp.pos.numpy(), inp.prompt_len.numpy(), inp.seq.numpy()
     mode = cfg.modes[0]
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
     done, t0 = 0, time.time()
-    while True:
-        O.decode_attention(*args, W=cfg.W, B=cfg.B, G=cfg.G, mode=mode)
-        done += 1
-        if time.time() - t0 >= budget_s:
-            break
+    try:
+        if ctx is not None:
+            ctx.__enter__()
+        while time.time() - t0 < budget_s:
+            O.decode_attention(q, K, V, pos, prompt, seq, W=cfg.W, B=cfg.B, G=cfg.G, mode=mode,
+                               queries=[done % inp.n_q])
+            done += 1
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
     dt = time.time() - t0
-    return {"value": round(done * inp.n_q / dt, 3), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{done} pass(es) over all {inp.n_q} queries x {cfg.hq} heads of {cfg.name} "
-                      f"({O.__name__} fp64 numpy, {dt:.1f}s wall)"}
+    return {"value": round(done / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": f"{done} queries (all {cfg.hq} heads each) of {cfg.name}, "
+                      f"{wl.MODE_NAMES[mode]} mask, taken in order, {dt:.1f}s wall; "
+                      f"{O.__name__} fp64 numpy, BLAS held to one thread"}
 
 
 def traffic_from_profile(workload):
@@ -396,7 +421,7 @@ def kernel_sha(paths):
 
 DECODE_SRC = [os.path.join(ROOT, "ar_image_generation_amd", "csrc", f)
               for f in ("decode.hip", "common.h")]
-PROBE_BYTES = 256 << 20
+PROBE_BYTES = 1 << 30
 
 
 def graph_us(torch, fn, n, steps, warmup):
@@ -562,7 +587,13 @@ def profile_run(args):
     b = DecodeBench(cfg, split=args.split)
     burn_in([b.k, b.v], 0.5)
     us = b.time_graph(cfg.modes[0], args.steps, args.warmup, path="fused")
+    # counter calibration: a streaming read of PROBE_BYTES that are not in
+    # any cache -- written, then pushed out of the L2s and the Infinity
+    # Cache by writing as many other bytes -- read once
     buf = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    evict = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    del evict
     sink = torch.empty(4096, dtype=torch.int32, device="cuda")
     da.hbm_read_probe(buf, sink, 2048)
     torch.cuda.synchronize()
@@ -638,7 +669,8 @@ def summarize(args):
         f"achieved_GBps_from_avg = {kept_bytes / avg if durs else float('nan'):.1f}",
         f"fetch_kib_per_dispatch = {f_dec}",
         f"write_kib_per_dispatch = {w_dec}",
-        f"probe_fetch_kib = {f_probe} (read of {PROBE_BYTES} bytes)",
+        f"probe_fetch_kib = {f_probe} (cold read of {PROBE_BYTES} bytes, written then evicted by "
+        f"another {PROBE_BYTES} bytes of writes)",
         f"fetch_scale = {scale}",
         f"write_calibration_kib = {w_fill} (fill of {PROBE_BYTES} bytes)",
         f"write_scale = {wscale}",
@@ -740,7 +772,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llamagen_b16")
+    ap.add_argument("--workload", default="paged_b128",
+                    help="headline decode workload (default: the largest, paged_b128)")
     ap.add_argument("--split", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip everything but the headline step, its dense run and the probe")
@@ -837,11 +870,26 @@ def main():
             del rb
             torch.cuda.empty_cache()
 
+    # the headline workload's other sparse mode(s)
+    other_modes = {}
+    for md in cfg.modes[1:]:
+        if md == da.DENSE:
+            continue
+        st = b.time_graph(md, K, W, path="fused")
+        gb = b.kept_bytes(md) / (st * 1e-6) / 1e9
+        other_modes[wl.MODE_NAMES[md]] = {
+            "us_per_step": round(st, 2), "tokens_per_s": round(b.n_q / (st * 1e-6), 1),
+            "kept_MB": round(b.kept_bytes(md) / 1e6, 2), "kept_GBps": round(gb, 1),
+            "frac_hbm_peak": round(gb / HBM_PEAK_GBPS, 4),
+            "speedup_vs_dense": round(us_step_d / st, 3)}
+        log(f"[bench] {cfg.name} {wl.MODE_NAMES[md]}: fused {st:.2f} us/step ({gb:.0f} GB/s)")
+
     extra = {}
     if not args.no_extra:
-        for name in ("gqa_b64", "paged_b128"):
+        for name in [n for n in ("llamagen_b16", "gqa_b64", "paged_b128") if n != cfg.name]:
             c = wl.CONFIGS[name]
             eb = DecodeBench(c)
+            burn_in([eb.k, eb.v], 0.3)
             rec = {}
             for md in list(dict.fromkeys(list(c.modes) + [da.DENSE])):
                 st = eb.time_graph(md, K, W, path="fused")
@@ -860,6 +908,11 @@ def main():
             for md in c.modes:
                 r = rec[wl.MODE_NAMES[md]]
                 r["speedup_vs_dense"] = round(dense_us / r["us_per_step"], 3)
+            pu, _ = attainable_read(eb.kept_bytes(c.modes[0]), K, W)
+            rec["attainable"] = {"us": round(pu, 3),
+                                 "GBps": round(eb.kept_bytes(c.modes[0]) / pu / 1e3, 1),
+                                 "step_frac_of_attainable": round(
+                                     pu / rec[wl.MODE_NAMES[c.modes[0]]]["us_per_step"], 4)}
             extra[name] = rec
             del eb
             torch.cuda.empty_cache()
@@ -888,9 +941,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded correlated-field K/V, random positions)",
+        "data": "synthetic (seeded correlated-field K/V, random positions; paged caches use a "
+                "seeded random block table)",
         "config": {"workload": cfg.name, "requests": cfg.n_seq, "q_heads": cfg.hq,
-                   "kv_heads": cfg.hkv, "head_dim": cfg.hd, "prompt": cfg.prompt[0],
+                   "kv_heads": cfg.hkv, "head_dim": cfg.hd, "prompt": list(cfg.prompt),
+                   "page_size": cfg.page_size,
                    "grid": cfg.G, "W": cfg.W, "B": cfg.B, "mode": wl.MODE_NAMES[mode],
                    "split": b.split, "dense_split": cfg.dense_split, "cache_copies": b.n_copies,
                    "step": "sparse_decode_attn_masked (keep-set build, lists written, and "
@@ -920,6 +975,7 @@ def main():
                   "kept_MB": round(b.kept_bytes(da.DENSE) / 1e6, 2),
                   "speedup_step": round(us_step_d / us_step, 3),
                   "speedup_decode": round(us_dec_d / us_dec, 3)},
+        "other_modes": other_modes,
         "extra": extra,
         "kv_residency": residency,
         "mask_sweep": sweep,

@@ -87,30 +87,43 @@ int64_t da_keep_count(const da_mask* m, int32_t pos, int32_t prompt_len, int32_t
  * and prompt_len <= max_prompt (n_keys as above); use it to size `cap`. */
 int64_t da_keep_cap(const da_mask* m, int32_t max_pos, int32_t max_prompt, int32_t n_keys);
 
-/* keepset_build -- per-query KV index lists and their maximal runs.
+/* keepset_build -- per-query KV index lists, their maximal runs and the
+ * split-KV tile list.
  *
  * For each query q < n_q at position pos[q] with prompt_len[q] tokens of
  * prompt, writes its keep-set (rule above) as ascending positions:
- *   count[q]              number of kept keys (the true size, even if > cap)
+ *   count[q]              number of kept keys (the true size, even if > cap;
+ *                         saturated at INT32_MAX)
  *   idx[q*cap + r]        r-th kept position, for r < min(count[q], cap)
  *   n_runs[q]             number of maximal runs of consecutive positions
  *   runs[(q*max_runs + k)*2 + {0,1}] = (first position, length) of run k,
  *                         for k < min(n_runs[q], max_runs)
- * runs/n_runs may both be NULL (then max_runs is ignored).  Entries of idx
- * and runs past count / n_runs are left untouched.
+ *   tiles[e*2 + {0,1}]    = (query, first entry) of tile e: each query's
+ *                         first min(count[q], cap) entries cut into
+ *                         consecutive chunks of `tile` entries, queries in
+ *                         order (the work list of a split-KV decode with
+ *                         split = tile), for e < min(*n_tiles, cap_tiles)
+ *   *n_tiles              total number of tiles (int64, the true total)
+ * runs/n_runs may both be NULL (then max_runs is ignored), and so may
+ * tiles/n_tiles (then tile and cap_tiles are ignored).  Entries of idx,
+ * runs and tiles past count / n_runs / n_tiles are left untouched.  The
+ * summary page's custom kernels work on tiles of the kept entries (section
+ * "技术方法详解", item 4); the tile list is that decomposition.
  *
  * Preconditions on device data: 0 <= pos[q]; 0 <= prompt_len[q]; for
  * causal = 0 also pos[q] < n_keys.  Queries that break them get count 0.
  * Overflow is reported, never written: if count[q] > cap (or n_runs[q] >
- * max_runs) the caller's list for q is truncated and must be treated as an
- * error (da_keep_cap gives a safe cap).
+ * max_runs, or *n_tiles > cap_tiles) the caller's list is truncated and
+ * must be treated as an error (da_keep_cap gives a safe cap).
  * Errors: DA_EINVAL for null required pointers, n_q < 0, cap < 1, W/B < 0,
  * G < 1, mode or causal out of range, causal = 0 with n_keys < 1,
- * runs/n_runs given with max_runs < 1 or only one of them given. */
+ * runs/n_runs given with max_runs < 1 or only one of them given,
+ * tiles/n_tiles given with tile < 1 or cap_tiles < 0 or only one given. */
 int da_keepset_build(const da_mask* m /* [host] */, int32_t n_q,
                      const int32_t* pos, const int32_t* prompt_len, int32_t n_keys,
                      int32_t cap, int32_t* count, int32_t* idx,
                      int32_t max_runs, int32_t* n_runs, int32_t* runs,
+                     int32_t tile, int32_t* tiles, int64_t cap_tiles, int64_t* n_tiles,
                      void* stream);
 
 /* KV cache descriptor: one form for contiguous and paged caches.
@@ -203,11 +216,17 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
  *   count, idx  optional outputs (both or neither): the lists exactly as
  *          da_keepset_build writes them (count[q] the true size; idx[q*cap+r]
  *          for r < min(count[q], cap)), for callers that reuse them
- *   head_wb optional [hkv][2] int32: a window and band (W, B) per kv head,
- *          replacing m->W, m->B for that head (adaptive / per-head budgets;
- *          negative values read as 0).  The query heads of a kv head share
- *          its keep-set, so each kept row is still read once.  Not allowed
- *          with count/idx (those lists are per query).
+ *   head_wb optional [hq][2] int32: a window and band (W, B) per query
+ *          head, replacing m->W, m->B for that head (per-head budgets and
+ *          windows adapted to the content, as the summary page's future
+ *          directions and the HeadKV abstract propose; negative values read
+ *          as 0).  The query heads of one kv head read the keep-set of the
+ *          group's widest (max W, max B) once -- it contains every head's,
+ *          both rules growing with W and B -- and each head masks the rows
+ *          outside its own keep-set, so a kept row is still read once per kv
+ *          head; `cap` must bound that widest keep-set.  Groups of 2, 4 or 8
+ *          query heads need bf16 (DA_ENOTSUP otherwise); with hq == hkv any
+ *          dtype.  Not allowed with count/idx (those lists are per query).
  *   k_new, v_new optional inputs (both or neither) [n_q][hkv][head_dim] in
  *          `dtype`, 16-byte aligned: KV append.  The row of each query's own
  *          position pos[q] is written into the cache (kv->k, kv->v, which must
@@ -223,7 +242,7 @@ int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
  * Errors: as da_sparse_decode_attn, plus DA_EINVAL for an invalid mask, null
  * pos/prompt_len, only one of count/idx or of k_new/v_new given, head_wb
  * together with count/idx, or misaligned k_new/v_new; DA_ENOTSUP for
- * causal = 0. */
+ * causal = 0 or head_wb with fp32 groups of query heads. */
 int da_sparse_decode_attn_masked(const da_mask* m /* [host] */, const void* q,
                                  da_dtype dtype, int32_t n_q, int32_t hq, int32_t hkv,
                                  int32_t head_dim, float scale,
@@ -314,7 +333,11 @@ int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t
  *   strides[12] [host]: element strides (batch, head, position) of q, k, v,
  *          out, in that order, each a multiple of 8;
  *   prompt_len [batch] (device; read clamped to [0, n]);
+ *   tiles, tiles_bytes: the lists of da_prefill_tiles_build for this mask, n
+ *          and prompt_len, and the size of that buffer (at least
+ *          da_prefill_tiles_bytes(batch, n));
  *   lse [batch][heads][n] fp32 natural-log sums, or NULL.
+ * W and B of n or more are read as n (no row/key distance reaches n).
  * Scores accumulate in fp32 from bf16 products; probabilities are rounded to
  * bf16 for the second product; outputs round to nearest even.  Tile entries
  * and counts are clamped into range, so an inconsistent list gives wrong
@@ -325,12 +348,14 @@ int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t
  * within a 64-key tile).
  * Errors: DA_EINVAL (mask, null pointers, sizes, strides, alignment),
  * DA_ENOTSUP (causal = 0, dtype other than bf16, head_dim not 64/128,
- * n > 65536, ROWDIAG with G > 1024, k/v position stride too large). */
+ * n > 65536, ROWDIAG with G > 1024, k/v position stride too large),
+ * DA_ECAPACITY (tiles_bytes below da_prefill_tiles_bytes(batch, n)). */
 int da_band_prefill_attn(const da_mask* m /* [host] */, da_dtype dtype, int32_t batch,
                          int32_t heads, int32_t kv_heads, int32_t n, int32_t head_dim,
                          const void* q, const void* k, const void* v, void* out,
                          const int64_t* strides /* [host] 12 */, const int32_t* prompt_len,
-                         const void* tiles, float scale, float* lse, void* stream);
+                         const void* tiles, int64_t tiles_bytes, float scale, float* lse,
+                         void* stream);
 
 /* Measurement: streaming read of `bytes` bytes at `buf` (16-byte aligned, a
  * multiple of 16) by `grid` workgroups of 256 threads, 16-byte loads, eight

@@ -70,18 +70,25 @@ def test_argument_errors_are_reported_before_launch():
     lib = da.load()
     m = da.mask(O.ROWDIAG, 4, 1, 3)
     dummy = ctypes.c_void_p(16)   # never dereferenced: checks fail first
-    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 0, dummy, dummy, 0, None, None, None)
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 0, dummy, dummy, 0, None, None, 0, None, 0, None, None)
     assert rc == -1 and "cap" in _native.last_error()
-    rc = lib.da_keepset_build(m, -1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, None)
+    rc = lib.da_keepset_build(m, -1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None)
     assert rc == -1
-    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 2, None, dummy, None)
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 2, None, dummy, 0, None, 0, None, None)
     assert rc == -1 and "both" in _native.last_error()
     bad = da.mask(O.BAND, -1, 1, 3)
-    assert lib.da_keepset_build(bad, 1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, None) == -1
+    assert lib.da_keepset_build(bad, 1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None) == -1
     nc = da.mask(O.BAND, 1, 1, 3, causal=False)
-    assert lib.da_keepset_build(nc, 1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, None) == -1
+    assert lib.da_keepset_build(nc, 1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None) == -1
     # zero queries is a valid no-op
-    assert lib.da_keepset_build(m, 0, None, None, 0, 4, None, None, 0, None, None, None) == 0
+    assert lib.da_keepset_build(m, 0, None, None, 0, 4, None, None, 0, None, None, 0, None, 0, None, None) == 0
+    # tile list: both pointers or neither, tile >= 1, cap_tiles >= 0
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 8, dummy, 4, None, None)
+    assert rc == -1 and "both" in _native.last_error()
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 0, dummy, 4, dummy, None)
+    assert rc == -1 and "tile" in _native.last_error()
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 8, dummy, -1, dummy, None)
+    assert rc == -1 and "cap_tiles" in _native.last_error()
 
     kv = _native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None, 1, 1, 8)
 
@@ -128,7 +135,7 @@ def test_prefill_limits_are_reported_before_launch():
 
     def pf(mk, n=1024, hd=128, dtype=1):
         return lib.da_band_prefill_attn(mk, dtype, 1, 2, 2, n, hd, dummy, dummy, dummy, dummy,
-                                        strides, dummy, dummy, 0.1, None, None)
+                                        strides, dummy, dummy, 1 << 30, 0.1, None, None)
     rd = da.mask(O.ROWDIAG, 64, 1, 32)
     assert pf(rd, n=70000) == -2 and "65536" in _native.last_error()
     assert pf(da.mask(O.ROWDIAG, 64, 1, 2048)) == -2 and "G <=" in _native.last_error()
@@ -140,8 +147,13 @@ def test_prefill_limits_are_reported_before_launch():
     big = (ctypes.c_int64 * 12)(*([128 * 1024, 128 * 1024, 128] * 4))
     big[5] = 34088000                  # k position stride: a 64-row tile spans > 4 GiB
     assert lib.da_band_prefill_attn(rd, 1, 1, 2, 2, 1024, 128, dummy, dummy, dummy, dummy, big,
-                                    dummy, dummy, 0.1, None, None) == -2
+                                    dummy, dummy, 1 << 30, 0.1, None, None) == -2
     assert "stride too large" in _native.last_error()
+    # a tile-list buffer smaller than the sizes need is refused
+    need = lib.da_prefill_tiles_bytes(1, 1024)
+    assert lib.da_band_prefill_attn(rd, 1, 1, 2, 2, 1024, 128, dummy, dummy, dummy, dummy, strides,
+                                    dummy, dummy, need - 1, 0.1, None, None) == -3
+    assert "tiles buffer" in _native.last_error()
 
 
 def test_decode_workspace_size():

@@ -310,38 +310,47 @@ def test_random_configurations(seed):
         assert_close(b[0], b[1], ref_o, ref_l, cfg.dtype)
 
 
-@pytest.mark.parametrize("split", [32, 4096])
-def test_per_head_masks(split):
-    """A (W, B) per kv head: each group of query heads against the oracle run
-    with its kv head's mask; with the same (W, B) everywhere, bitwise the
-    shared-mask call."""
-    cfg = wl.small_decode("gqa_b64", n_seq=3)
-    inp = wl.decode_inputs(cfg)
-    k, v, bt = caches(inp)
-    rng = np.random.default_rng(7)
-    wb = np.stack([rng.integers(0, 300, cfg.hkv), rng.integers(0, 7, cfg.hkv)], axis=1).astype(np.int32)
-    head_wb = torch.from_numpy(wb).to(dev())
-    args = (inp.q.to(dev()), k, v, inp.seq.to(dev()), inp.pos.to(dev()), inp.prompt_len.to(dev()))
-    maxpos, maxp = int(inp.pos.max()), int(inp.prompt_len.max())
+def _per_head_reference(inp, wb, mode):
+    """The oracle once per query head, with that head's (W, B)."""
+    cfg = inp.cfg
     grp = cfg.hq // cfg.hkv
     q = inp.q.double().numpy()
     K, V = inp.k_logical.double().numpy(), inp.v_logical.double().numpy()
+    ref_o = np.zeros(q.shape)
+    ref_l = np.zeros(q.shape[:2])
+    for h, (w, b) in enumerate(wb):
+        g = h // grp
+        o_h, l_h = O.decode_attention(q[:, h:h + 1], K[:, g:g + 1], V[:, g:g + 1], inp.pos.numpy(),
+                                      inp.prompt_len.numpy(), inp.seq.numpy(),
+                                      W=int(w), B=int(b), G=cfg.G, mode=mode)
+        ref_o[:, h:h + 1], ref_l[:, h:h + 1] = o_h, l_h
+    return ref_o, ref_l
+
+
+@pytest.mark.parametrize("name,split", [("gqa_b64", 32), ("gqa_b64", 4096), ("paged_b128", 4096),
+                                        ("llamagen_b16", 4096)])
+def test_per_head_masks(name, split):
+    """A (W, B) per query head (heads of one kv group differ): every head
+    against the oracle run with its own mask.  The group reads its widest
+    keep-set once and masks per head, so GQA sharing is kept; MHA reads per
+    head.  With the same (W, B) everywhere, bitwise the shared-mask call."""
+    cfg = wl.small_decode(name, n_seq=3)
+    inp = wl.decode_inputs(cfg)
+    k, v, bt = caches(inp)
+    rng = np.random.default_rng(7)
+    wb = np.stack([rng.integers(0, 300, cfg.hq), rng.integers(0, 7, cfg.hq)], axis=1).astype(np.int32)
+    head_wb = torch.from_numpy(wb).to(dev())
+    args = (inp.q.to(dev()), k, v, inp.seq.to(dev()), inp.pos.to(dev()), inp.prompt_len.to(dev()))
+    maxpos, maxp = int(inp.pos.max()), int(inp.prompt_len.max())
     for mode in (O.BAND, O.ROWDIAG):
         m = da.mask(mode, cfg.W, cfg.B, cfg.G)
-        cap = max(da.keep_cap(da.mask(mode, int(w), int(b), cfg.G), maxpos, maxp) for w, b in wb)
+        cap = da.keep_cap(m, maxpos, maxp, head_wb=wb)
         out, lse, _, _ = da.sparse_decode_attn_masked(m, *args, cap=cap, split=split, block_table=bt,
                                                       want_lse=True, head_wb=head_wb)
         torch.cuda.synchronize()
-        ref_o = np.zeros(q.shape)
-        ref_l = np.zeros(q.shape[:2])
-        for g, (w, b) in enumerate(wb):
-            hs = slice(g * grp, (g + 1) * grp)
-            o_g, l_g = O.decode_attention(q[:, hs], K[:, g:g + 1], V[:, g:g + 1], inp.pos.numpy(),
-                                          inp.prompt_len.numpy(), inp.seq.numpy(),
-                                          W=int(w), B=int(b), G=cfg.G, mode=mode)
-            ref_o[:, hs], ref_l[:, hs] = o_g, l_g
+        ref_o, ref_l = _per_head_reference(inp, wb, mode)
         assert_close(out.cpu(), lse.cpu(), ref_o, ref_l, cfg.dtype)
-    same = torch.tensor([[cfg.W, cfg.B]] * cfg.hkv, dtype=torch.int32, device=dev())
+    same = torch.tensor([[cfg.W, cfg.B]] * cfg.hq, dtype=torch.int32, device=dev())
     m = da.mask(O.ROWDIAG, cfg.W, cfg.B, cfg.G)
     cap = da.keep_cap(m, maxpos, maxp)
     o1, l1, _, _ = da.sparse_decode_attn_masked(m, *args, cap=cap, split=split, block_table=bt,
@@ -350,6 +359,41 @@ def test_per_head_masks(split):
                                                 want_lse=True)
     torch.cuda.synchronize()
     assert torch.equal(o1.cpu(), o2.cpu()) and torch.equal(l1.cpu(), l2.cpu())
+
+
+def test_sink_plus_window_mode():
+    """StreamingLLM-style attention sinks plus a recent window is the band
+    mode with the sinks as the prompt and B >= W: it keeps exactly keys
+    j < P and i - W <= j <= i.  Against the oracle, and the keep-set against
+    that closed description."""
+    cfg = wl.small_decode("gqa_b64", n_seq=4, prompt=(4, 4), W=200, B=200)
+    inp = wl.decode_inputs(cfg)
+    for i, P in zip(inp.pos.tolist(), inp.prompt_len.tolist()):
+        ks = O.keepset(int(i), P=int(P), W=200, B=200, G=cfg.G, mode=O.BAND)
+        want = sorted(set(range(min(P, i + 1))) | set(range(max(0, i - 200), i + 1)))
+        assert ks.tolist() == want
+    k, v, bt = caches(inp)
+    m = da.mask(O.BAND, 200, 200, cfg.G)
+    cap = da.keep_cap(m, int(inp.pos.max()), int(inp.prompt_len.max()))
+    out, lse, _, _ = da.sparse_decode_attn_masked(m, inp.q.to(dev()), k, v, inp.seq.to(dev()),
+                                                  inp.pos.to(dev()), inp.prompt_len.to(dev()), cap=cap,
+                                                  split=4096, block_table=bt, want_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_l = run_oracle(inp, O.BAND)
+    assert_close(out.cpu(), lse.cpu(), ref_o, ref_l, cfg.dtype)
+
+
+def test_per_head_masks_fp32_groups_not_supported():
+    cfg = wl.small_decode("gqa_b64", n_seq=1, dtype="f32")
+    inp = wl.decode_inputs(cfg)
+    k, v, bt = caches(inp)
+    wb = torch.tensor([[cfg.W, cfg.B]] * cfg.hq, dtype=torch.int32, device=dev())
+    m = da.mask(O.ROWDIAG, cfg.W, cfg.B, cfg.G)
+    with pytest.raises(da.DiagAttnError) as e:
+        da.sparse_decode_attn_masked(m, inp.q.to(dev()), k, v, inp.seq.to(dev()), inp.pos.to(dev()),
+                                     inp.prompt_len.to(dev()), cap=2000, split=4096, block_table=bt,
+                                     head_wb=wb)
+    assert e.value.status == -2
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -20,7 +20,9 @@ def build(mode, W, B, G, pos, prompt, cap, causal=True, n_keys=0, max_runs=64):
     count, idx, n_runs, runs = da.keepset_build(m, pos_t, pr_t, cap, n_keys=n_keys,
                                                 max_runs=max_runs)
     torch.cuda.synchronize()
-    return count.cpu().numpy(), idx.cpu().numpy(), n_runs.cpu().numpy(), runs.cpu().numpy()
+    return (count.cpu().numpy(), idx.cpu().numpy(),
+            None if n_runs is None else n_runs.cpu().numpy(),
+            None if runs is None else runs.cpu().numpy())
 
 
 def check(mode, W, B, G, pos, prompt, causal=True, n_keys=0, cap=None):
@@ -116,3 +118,101 @@ def test_capacity_overflow_is_reported_not_written():
 def test_invalid_device_positions_give_empty_sets():
     count, _, n_runs, _ = build(O.ROWDIAG, 8, 1, 4, [-1, 5, 3], [0, -2, 2], 16)
     assert count.tolist() == [0, 0, 4] and n_runs[:2].tolist() == [0, 0]
+
+
+def _tiles(mode, W, B, G, pos, prompt, cap, tile, cap_tiles, causal=True, n_keys=0):
+    m = da.mask(mode, W, B, G, causal)
+    pos_t = torch.as_tensor(np.asarray(pos), dtype=torch.int32).to(DEV)
+    pr_t = torch.as_tensor(np.asarray(prompt), dtype=torch.int32).to(DEV)
+    count, idx, tiles, n_tiles = da.keepset_tiles(m, pos_t, pr_t, cap, tile, cap_tiles,
+                                                  n_keys=n_keys)
+    torch.cuda.synchronize()
+    return count.cpu().numpy(), tiles.cpu().numpy(), int(n_tiles.item())
+
+
+@pytest.mark.parametrize("name,tile", [("sweep_f32", 8), ("llamagen_b16", 64), ("gqa_b64", 96),
+                                       ("paged_b128", 100), ("paged_b128", 1)])
+def test_tile_list_bit_exact(name, tile):
+    """The split-KV tile list equals oracle.tiles over the oracle's counts."""
+    cfg = wl.CONFIGS[name]
+    pos, prompt, _ = wl.positions(cfg)
+    pos, prompt = pos.numpy(), prompt.numpy()
+    for mode in set(cfg.modes) | {O.DENSE}:
+        counts = [len(O.keepset(int(i), P=int(P), W=cfg.W, B=cfg.B, G=cfg.G, mode=mode))
+                  for i, P in zip(pos, prompt)]
+        want = O.tiles(counts, tile)
+        cap = max(counts)
+        _, tiles, n_tiles = _tiles(mode, cfg.W, cfg.B, cfg.G, pos, prompt, cap, tile, len(want) + 5)
+        assert n_tiles == len(want)
+        assert np.array_equal(tiles[:n_tiles], want)
+
+
+def test_tile_list_many_queries_and_truncation():
+    """Several 1024-query rounds of the scan; a cap below some counts cuts
+    those lists (tiles cover min(count, cap)); a short tile buffer is filled
+    exactly to its end and the true total is still reported."""
+    rng = np.random.default_rng(11)
+    n = 2500
+    prompt = rng.integers(0, 50, size=n)
+    pos = prompt + rng.integers(0, 300, size=n)
+    W, B, G, cap, tile = 96, 2, 32, 60, 16
+    counts = [min(cap, len(O.keepset(int(i), P=int(P), W=W, B=B, G=G, mode=O.ROWDIAG)))
+              for i, P in zip(pos, prompt)]
+    want = O.tiles(counts, tile)
+    _, tiles, n_tiles = _tiles(O.ROWDIAG, W, B, G, pos, prompt, cap, tile, len(want))
+    assert n_tiles == len(want) and np.array_equal(tiles, want)
+    short = len(want) // 3
+    m = da.mask(O.ROWDIAG, W, B, G)
+    buf = torch.full((short + 10, 2), -5, dtype=torch.int32, device=DEV)
+    nt = torch.zeros(1, dtype=torch.int64, device=DEV)
+    da.keepset_tiles(m, torch.as_tensor(pos, dtype=torch.int32).to(DEV),
+                     torch.as_tensor(prompt, dtype=torch.int32).to(DEV), cap, tile, short,
+                     tiles=buf, n_tiles=nt)
+    torch.cuda.synchronize()
+    assert int(nt.item()) == len(want)
+    got = buf.cpu().numpy()
+    assert np.array_equal(got[:short], want[:short]) and (got[short:] == -5).all()
+
+
+def test_tile_list_of_no_queries():
+    m = da.mask(O.ROWDIAG, 8, 1, 4)
+    e = torch.empty(0, dtype=torch.int32, device=DEV)
+    _, _, tiles, nt = da.keepset_tiles(m, e, e, 4, 8, 4)
+    torch.cuda.synchronize()
+    assert int(nt.item()) == 0
+
+
+def test_matrix_form_extreme_parameters():
+    """Non-causal matrix form with B, W at INT32_MAX: the window end i + B
+    and the scan stay exact (64-bit); lists equal the scalar predicate's
+    (oracle.keepset_loop: every pair tested, no closed form)."""
+    big = 2**31 - 1
+    n_keys = 300
+    for (mode, W, B, G) in [(O.BAND, big, big, 1), (O.ROWDIAG, big, big, 7), (O.ROWDIAG, 40, big, 5),
+                            (O.BAND, 3, big, 1), (O.ROWDIAG, big, 2, 9)]:
+        pos = np.array([0, 1, 150, 299])
+        prompt = np.array([0, 5, 20, 300])
+        count, idx, _, _ = build(mode, W, B, G, pos, prompt, n_keys, causal=False, n_keys=n_keys)
+        m = da.mask(mode, W, B, G, causal=False)
+        for q in range(pos.size):
+            ks = O.keepset_loop(int(pos[q]), n_keys, P=int(prompt[q]), W=W, B=B, G=G, mode=mode,
+                                causal=False)
+            assert count[q] == len(ks), (mode, W, B, G, q)
+            assert idx[q, :count[q]].tolist() == ks
+            assert count[q] == da.keep_count(m, int(pos[q]), int(prompt[q]), n_keys)
+
+
+def test_causal_counts_at_the_top_of_the_int32_range():
+    """Queries at positions near INT32_MAX (only counts: the lists would be
+    too long to hold).  With P = 0 and a finite window the count depends
+    only on the window, so the oracle's count at a small position past the
+    window is the reference; a window covering everything keeps i + 1 keys,
+    which saturates at INT32_MAX."""
+    big = 2**31 - 1
+    top = np.array([big, big - 1, big - 63, big - 64])
+    for (mode, W, B, G) in [(O.BAND, 100, 7, 1), (O.ROWDIAG, 96, 2, 32), (O.ROWDIAG, 50, 30, 16)]:
+        ref = len(O.keepset(W + 5, P=0, W=W, B=B, G=G, mode=mode))
+        count, _, _, _ = build(mode, W, B, G, top, np.zeros(4, dtype=np.int64), 8, max_runs=0)
+        assert count.tolist() == [ref] * 4, (mode, W, B, G)
+    count, _, _, _ = build(O.DENSE, 0, 0, 1, top, np.zeros(4, dtype=np.int64), 8, max_runs=0)
+    assert count.tolist() == [big, big, big - 62, big - 63]
