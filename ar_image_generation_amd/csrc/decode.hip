@@ -769,8 +769,8 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
       }
     }
   }
-  const char* kb = reinterpret_cast<const char*>(k_p) + ((int64_t)g * a.head_stride + 8 * lg) * 2;
-  const char* vb = reinterpret_cast<const char*>(v_p) + ((int64_t)g * a.head_stride + 8 * lg) * 2;
+  const char* kb = reinterpret_cast<const char*>(k_p) + (int64_t)g * a.head_stride * 2;
+  const char* vb = reinterpret_cast<const char*>(v_p) + (int64_t)g * a.head_stride * 2;
 
   int cnt, nrows;
   const int sq = clampi(sq_m, 0, a.n_seq - 1);
@@ -879,8 +879,8 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
   }
 
   // B operand chunk c of S^T = K Q^T: query head l % 16, dims 32c + 8 (l / 16)
-  auto qop = [&](int c, int zo) {
-    return *reinterpret_cast<const bf16x8*>(qsh + zo + lr * HD + (((4 * c + lg) ^ swz<CPR>(lr)) * 8));
+  auto qop = [&](int c, int lr_, int lg_) {
+    return *reinterpret_cast<const bf16x8*>(qsh + lr_ * HD + (((4 * c + lg_) ^ swz<CPR>(lr_)) * 8));
   };
   // KV append: scores of the new K row for this lane's query head, on the
   // matrix core with the same operand layout as every block's rows
@@ -890,7 +890,7 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
       f32x4 sn = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        sn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, newrow[4 * c + lg]), qop(c, 0),
+        sn = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, newrow[4 * c + lg]), qop(c, lr, lg),
                                                      sn, 0, 0, 0);
       s_new = sn[0];
     }
@@ -906,25 +906,37 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
   for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One K and one V buffer: the next block's K is issued as soon as this
-  // block's scores are out, its V once this block's V is staged, so every
-  // wave has a block of loads in flight while it computes; sixteen waves a
-  // CU then hold 128 KiB of reads in flight
+  // block's K is staged, its V once this block's V is staged, so every wave
+  // has a block of loads in flight while it computes; sixteen waves a CU
+  // then hold 128 KiB of reads in flight.  Loads are whole rows, RPI rows an
+  // instruction (lane l: row c RPI + l / CPR, 16-byte chunk l % CPR): rows
+  // read in 64-byte pieces, as the matrix-core operand layout would have
+  // them, measured 28 % slower on the same data.
+  constexpr int RPI = 64 / CPR;
+  const int nrow_l = lane / CPR, nchk_l = lane % CPR;
   u32x4 kk[NC], vv[NC];
-  auto byte_off = [&](int blk) {
-    const int row = blk * 16 + lr;
-    return rowoff[row < nrows ? row : nrows - 1] * 2;
+  auto row_bytes = [&](int blk, int c) {
+    const int row = blk * 16 + c * RPI + nrow_l;
+    return rowoff[row < nrows ? row : nrows - 1] * 2 + nchk_l * 16;
   };
   auto load_k = [&](int blk) {
-    const int64_t off = byte_off(blk);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      kk[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + off + 64 * c));
+      kk[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kb + row_bytes(blk, c)));
   };
   auto load_v = [&](int blk) {
-    const int64_t off = byte_off(blk);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      vv[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + off + 64 * c));
+      vv[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + row_bytes(blk, c)));
+  };
+  // a block's rows as loaded to the wave's staging area, row-major with
+  // swizzled chunks
+  auto stage_rows = [&](uint16_t* st, const u32x4 (&x)[NC], int lane_) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int r = c * RPI + lane_ / CPR;
+      *reinterpret_cast<u32x4*>(st + r * HD + (((lane_ % CPR) ^ swz<CPR>(r)) * 8)) = x[c];
+    }
   };
   auto process = [&](int blk) {
     // LDS addresses (query operand, V staging, transposing reads) are taken
@@ -933,21 +945,29 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
     // loop (which spilled)
     int zo = 0;
     __asm__ volatile("" : "+v"(zo));
-    uint16_t* const vsw = vst + zo;
+    uint16_t* const vsw = vst;
+    // lane coordinates the compiler cannot see as loop-invariant: every LDS
+    // offset derived from them is recomputed per block (a few integer ops)
+    // instead of being held in registers through the loop
+    const int lane_z = lane + zo, lr_z = lane_z & 15, lg_z = lane_z >> 4;
+    // K through the staging area into the A operand of S^T = K Q^T (lane l:
+    // row l % 16, dims 32c + 8 (l / 16) .. + 8)
+    stage_rows(vsw, kk, lane_z);
+    // the refill of this K buffer stays behind the stores that read it (an
+    // empty asm that orders memory: hoisted above them, the loads would
+    // force a copy of the buffer and a wait for every load in flight)
+    __asm__ volatile("" ::: "memory");
+    load_k(blk + 4);
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kk[c]), qop(c, zo), sc, 0, 0, 0);
-    // the refill of this K buffer stays behind the products that read it:
-    // the empty asm takes their result and orders memory, so the scheduler
-    // can neither hoist the loads above the products (which would copy the
-    // buffer and wait for every load in flight) nor sink the products
-    __asm__ volatile("" : "+v"(sc)::"memory");
-    load_k(blk + 4);
-    // V to the wave's staging area, row-major with swizzled chunks
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      *reinterpret_cast<u32x4*>(vsw + lr * HD + (((4 * c + lg) ^ swz<CPR>(lr)) * 8)) = vv[c];
+    for (int c = 0; c < NC; ++c) {
+      const bf16x8 ka =
+          *reinterpret_cast<const bf16x8*>(vsw + lr_z * HD + (((4 * c + lg_z) ^ swz<CPR>(lr_z)) * 8));
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qop(c, lr_z, lg_z), sc, 0, 0, 0);
+    }
+    // V over the K rows (the operand reads above precede these stores: LDS
+    // operations of a wave run in order)
+    stage_rows(vsw, vv, lane_z);
     if constexpr (MASKED) {
       // KV append: the new token's row is row sub_row % 16 of its block.
       // Its V row goes over the staged one, and its scores are the ones
@@ -958,7 +978,7 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
         if (lr == rr) {
 #pragma unroll
           for (int c = 0; c < NC; ++c)
-            *reinterpret_cast<u32x4*>(vsw + lr * HD + (((4 * c + lg) ^ swz<CPR>(lr)) * 8)) =
+            *reinterpret_cast<u32x4*>(vsw + lr_z * HD + (((4 * c + lg_z) ^ swz<CPR>(lr_z)) * 8)) =
                 newrow[CPR + 4 * c + lg];
         }
 #pragma unroll
@@ -966,7 +986,7 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
       }
     }
     // likewise the refill of the V buffer stays behind its staging stores
-    __asm__ volatile("" ::: "memory");
+    __asm__ volatile("" : "+v"(sc)::"memory");
     load_v(blk + 4);
     float sv[4];
 #pragma unroll
@@ -1000,10 +1020,10 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
       pb[r] = __builtin_bit_cast(short, (__bf16)p);
     }
     // O^T += V^T P^T, one 16-dim block at a time
-    const int vr = 4 * lg + (lr >> 2);
+    const int vr = 4 * lg_z + (lr_z >> 2);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const uint16_t* pv = vsw + vr * HD + (((2 * nb + ((lr & 3) >> 1)) ^ swz<CPR>(vr)) * 8) + (lr & 1) * 4;
+      const uint16_t* pv = vsw + vr * HD + (((2 * nb + ((lr_z & 3) >> 1)) ^ swz<CPR>(vr)) * 8) + (lr_z & 1) * 4;
       const v4i16 av = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(pv));
       o[nb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pb, o[nb], 0, 0, 0);
     }
