@@ -22,4 +22,6 @@ from .api import (  # noqa: F401
     ring_pages,
     sparse_decode_attn,
     sparse_decode_attn_masked,
+    sparse_decode_attn_masked_noalloc,
+    decode_scratch_bytes,
 )

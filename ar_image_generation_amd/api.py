@@ -216,11 +216,34 @@ def sparse_decode_attn_masked(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
     Returns (out, lse or None, count or None, idx or None)."""
     return _decode_masked(m, q, k_cache, v_cache, seq, pos, prompt_len, cap, split, block_table,
                           scale, out, lse, want_lse, workspace, count, idx, want_lists, k_new,
-                          v_new, head_wb)
+                          v_new, head_wb, noalloc=False)
+
+
+def sparse_decode_attn_masked_noalloc(m: DaMask, q: torch.Tensor, k_cache: torch.Tensor,
+                                      v_cache: torch.Tensor, seq: torch.Tensor, pos: torch.Tensor,
+                                      prompt_len: torch.Tensor, *, cap: int, split: int, out,
+                                      block_table: Optional[torch.Tensor] = None,
+                                      scale: Optional[float] = None, lse=None, count=None,
+                                      idx=None, k_new=None, v_new=None, head_wb=None):
+    """``sparse_decode_attn_masked`` through the allocation-free entry point:
+    no workspace (the library's per-GPU scratch array serves instead) and no
+    output allocation (``out``, and ``lse``/``count``/``idx`` when wanted,
+    are the caller's).  Returns (out, lse, count, idx)."""
+    if out is None:
+        raise ValueError("sparse_decode_attn_masked_noalloc: pass `out` (nothing is allocated)")
+    return _decode_masked(m, q, k_cache, v_cache, seq, pos, prompt_len, cap, split, block_table,
+                          scale, out, lse, False, None, count, idx, False, k_new, v_new, head_wb,
+                          noalloc=True)
+
+
+def decode_scratch_bytes() -> int:
+    """Scratch bytes behind the allocation-free decode entry point."""
+    return int(load().da_decode_scratch_bytes())
 
 
 def _decode_masked(m, q, k_cache, v_cache, seq, pos, prompt_len, cap, split, block_table, scale,
-                   out, lse, want_lse, workspace, count, idx, want_lists, k_new, v_new, head_wb):
+                   out, lse, want_lse, workspace, count, idx, want_lists, k_new, v_new, head_wb,
+                   noalloc):
     _need_cuda("sparse_decode_attn_masked", q, k_cache, v_cache, seq, pos, prompt_len, block_table,
                k_new, v_new, head_wb, out, lse, count, idx)
     if q.dim() != 3 or not q.is_contiguous():
@@ -261,6 +284,13 @@ def _decode_masked(m, q, k_cache, v_cache, seq, pos, prompt_len, cap, split, blo
                             tuple(lse.shape) != (n_q, hq)):
         raise ValueError("lse must be a contiguous fp32 [n_q, hq] tensor")
     kv = kv_cache(k_cache, v_cache, block_table)
+    if noalloc:
+        check(load().da_sparse_decode_attn_masked_noalloc(
+                  m, _ptr(q), _DTYPE[q.dtype], n_q, hq, hkv, hd, float(scale), kv, _ptr(seq),
+                  _ptr(pos), _ptr(prompt_len), _ptr(head_wb), _ptr(k_new), _ptr(v_new), cap, split,
+                  _ptr(count), _ptr(idx), _ptr(out), _ptr(lse), _stream(q)),
+              "da_sparse_decode_attn_masked_noalloc")
+        return out, lse, count, idx
     if workspace is None:
         workspace = decode_workspace(n_q, hq, hd, cap, split, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -1384,6 +1384,46 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
   return launch_decode<0>(a, dtype, head_dim, stream);
 }
 
+namespace da {
+
+// Scratch memory of the allocation-free entry point: the decode workspace
+// (chunk partials and keep-set sizes) in a file-scope device array, one
+// copy per GPU, alive until the process ends.  Host code never uses the
+// array's name as an address: the device address of each GPU's copy comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+// This device's scratch address, or nullptr with the error recorded.
+static void* scratch_ptr() {
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    fail(DA_EHIP, "scratch: no current device (or device id >= %d)", kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      fail(DA_EHIP, "scratch: hipGetSymbolAddress: %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
+}  // namespace da
+
+extern "C" int64_t da_decode_scratch_bytes(void) { return kScratchBytes; }
+
 extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_dtype dtype,
                                             int32_t n_q, int32_t hq, int32_t hkv, int32_t head_dim,
                                             float scale, const da_kv_cache* kv, const int32_t* seq,
@@ -1429,3 +1469,27 @@ extern "C" int da_sparse_decode_attn_masked(const da_mask* m, const void* q, da_
                  : launch_decode<1>(a, dtype, head_dim, stream);
 }
 
+extern "C" int da_sparse_decode_attn_masked_noalloc(const da_mask* m, const void* q, da_dtype dtype,
+                                                    int32_t n_q, int32_t hq, int32_t hkv,
+                                                    int32_t head_dim, float scale,
+                                                    const da_kv_cache* kv, const int32_t* seq,
+                                                    const int32_t* pos, const int32_t* prompt_len,
+                                                    const int32_t* head_wb, const void* k_new,
+                                                    const void* v_new, int32_t cap, int32_t split,
+                                                    int32_t* count, int32_t* idx, void* out,
+                                                    float* lse, void* stream) {
+  if (n_q < 0 || hq < 1 || head_dim < 1 || cap < 1 || split < 1)
+    return fail(DA_EINVAL, "n_q=%d hq=%d head_dim=%d cap=%d split=%d", n_q, hq, head_dim, cap, split);
+  const int64_t need = ws_layout(n_q, hq, head_dim, n_splits(cap, split)).bytes;
+  if (need > kScratchBytes)
+    return fail(DA_ECAPACITY, "these sizes need %lld bytes of scratch; the allocation-free call has %lld",
+                (long long)need, (long long)kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && n_q > 0) {
+    ws = scratch_ptr();
+    if (!ws) return DA_EHIP;
+  }
+  return da_sparse_decode_attn_masked(m, q, dtype, n_q, hq, hkv, head_dim, scale, kv, seq, pos,
+                                      prompt_len, head_wb, k_new, v_new, cap, split, count, idx, out,
+                                      lse, ws, ws ? kScratchBytes : 0, stream);
+}

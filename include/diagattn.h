@@ -254,6 +254,39 @@ int da_sparse_decode_attn_masked(const da_mask* m /* [host] */, const void* q,
                                  void* out, float* lse, void* workspace, int64_t ws_bytes,
                                  void* stream);
 
+/* [host] Size in bytes of the scratch memory behind
+ * da_sparse_decode_attn_masked_noalloc (a fixed maximum, 32 MiB). */
+int64_t da_decode_scratch_bytes(void);
+
+/* sparse_decode_attn_masked_noalloc -- da_sparse_decode_attn_masked without
+ * a caller workspace and without any allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).
+ *
+ * Arguments, outputs and results are those of da_sparse_decode_attn_masked
+ * (the same kernels run).  The workspace it needs when a keep-set spans
+ * several chunks (cap > split) comes from a device array inside the library,
+ * da_decode_scratch_bytes() long, one per GPU, held until the process ends;
+ * its device address is looked up (not allocated) on the first call on each
+ * device.  No hipMalloc, hipFree or allocating library routine is called.
+ * The array keeps the last call's contents; nothing in it needs clearing
+ * between calls.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (concurrent streams, or host threads
+ * sharing a device) race: order them on one stream.
+ * Errors: as da_sparse_decode_attn_masked, plus DA_ECAPACITY when the
+ * sizes need more than da_decode_scratch_bytes() of workspace
+ * (da_decode_workspace_bytes(n_q, hq, head_dim, cap, split) > that), and
+ * DA_EHIP if the device address of the array cannot be obtained. */
+int da_sparse_decode_attn_masked_noalloc(const da_mask* m /* [host] */, const void* q,
+                                         da_dtype dtype, int32_t n_q, int32_t hq, int32_t hkv,
+                                         int32_t head_dim, float scale,
+                                         const da_kv_cache* kv /* [host] */, const int32_t* seq,
+                                         const int32_t* pos, const int32_t* prompt_len,
+                                         const int32_t* head_wb,
+                                         const void* k_new, const void* v_new,
+                                         int32_t cap, int32_t split, int32_t* count, int32_t* idx,
+                                         void* out, float* lse, void* stream);
+
 /* KV residency.  Under the keep-set rule a decode query at position i reads
  * prompt keys and keys j >= i - W (the summary's M, core formulas; BAND also
  * needs |i - j| <= B, so only j >= i - min(B, W)), and later queries only
