@@ -328,7 +328,7 @@ def ring_block_table(m: DaMask, prompt_len, max_len: int, page_size: int, first_
 
 
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int,
-                   nbytes: Optional[int] = None, offset: int = 0) -> None:
+                   nbytes: Optional[int] = None, offset: int = 0, loads_in_flight: int = 8) -> None:
     """Streams `nbytes` bytes of `buf` starting at byte `offset` (measurement)."""
     _need_cuda("hbm_read_probe", buf, sink)
     total = buf.numel() * buf.element_size()
@@ -336,7 +336,7 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int,
     if offset < 0 or offset + nbytes > total or sink.numel() < grid or sink.element_size() != 4:
         raise ValueError("hbm_read_probe: range outside the buffer or sink too small")
     check(load().da_hbm_read_probe(buf.data_ptr() + offset, nbytes, sink.data_ptr(), grid,
-                                   _stream(buf)),
+                                   int(loads_in_flight), _stream(buf)),
           "da_hbm_read_probe")
 
 

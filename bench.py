@@ -491,16 +491,19 @@ def mask_sweep(b, steps, warmup, w_rows=(1, 2, 3, 6), bands=(0, 1, 2, 4)):
 
 
 def per_head_run(b, steps, warmup):
-    """Per-kv-head windows at the benchmark shape: kv heads alternate between
-    a window of one raster row and of three (B unchanged), as a per-head
-    budget would set them.  Returns the step time and kept bytes."""
+    """Per-query-head windows at the benchmark shape: query heads alternate
+    between a window of one raster row and of three (B unchanged), as a
+    per-head budget would set them.  A kv group reads its widest keep-set
+    once and masks per head, so the bytes read are those of each group's
+    widest mask.  Returns the step time, the bytes read and, for reference,
+    the bytes of the per-head keep-sets themselves."""
     torch, da = b.torch, b.da
     cfg = b.cfg
-    wb = [[cfg.G * (1 if g % 2 == 0 else 3), cfg.B] for g in range(cfg.hkv)]
+    wb = [[cfg.G * (1 if h % 2 == 0 else 3), cfg.B] for h in range(cfg.hq)]
     head_wb = torch.tensor(wb, dtype=torch.int32, device=b.q.device)
     m = da.mask(cfg.modes[0], cfg.W, cfg.B, cfg.G)
     maxpos, maxp = int(b.inp.pos.max()), int(b.inp.prompt_len.max())
-    cap = max(da.keep_cap(da.mask(cfg.modes[0], w, bb, cfg.G), maxpos, maxp) for w, bb in wb)
+    cap = da.keep_cap(m, maxpos, maxp, head_wb=wb)
     out = torch.empty_like(b.q)
 
     def run(c):
@@ -509,10 +512,72 @@ def per_head_run(b, steps, warmup):
                                      head_wb=head_wb)
     us = graph_us(torch, run, b.n_copies, steps, warmup)
     row = 2 * cfg.hd * (2 if cfg.dtype == "bf16" else 4)
-    kept = sum(da.keep_count(da.mask(cfg.modes[0], w, bb, cfg.G), int(p), int(P))
-               for w, bb in wb for p, P in zip(*b.hosts)) * row
+    grp = cfg.hq // cfg.hkv
+
+    def count(w, bb):
+        return sum(da.keep_count(da.mask(cfg.modes[0], w, bb, cfg.G), int(p), int(P))
+                   for p, P in zip(*b.hosts))
+    read = sum(count(max(w for w, _ in wb[g * grp:(g + 1) * grp]),
+                     max(bb for _, bb in wb[g * grp:(g + 1) * grp])) for g in range(cfg.hkv)) * row
+    own = sum(count(w, bb) for w, bb in wb) * row / grp
     return {"head_W": [w for w, _ in wb], "us_per_step": round(us, 2),
-            "kept_MB": round(kept / 1e6, 3), "kept_GBps": round(kept / (us * 1e-6) / 1e9, 1)}
+            "read_MB": round(read / 1e6, 3), "per_head_keepset_MB": round(own / 1e6, 3),
+            "read_GBps": round(read / (us * 1e-6) / 1e9, 1)}
+
+
+def kv_budget_run(steps, warmup, base_requests=128, max_requests=2048, page_size=16):
+    """KV residency turned into batch size.  The HBM that a full paged cache
+    of `base_requests` requests of the paged workload takes (one page per 16
+    positions of each request's whole sequence) is the budget.  Under the
+    row-diagonal keep-set a request needs only its prompt pages plus a ring
+    of window pages (da.ring_pages), so the same budget holds many more
+    requests: the largest batch whose ring pages fit is decoded through the
+    ring block table (one query per request, position uniform over the
+    image as in the workload), and its step time and tokens/s are reported
+    beside the full-cache batch's.  Values are random: time depends only on
+    the keep-sets.  Returns the record."""
+    import numpy as np
+    import torch
+    import ar_image_generation_amd as da
+    import workloads as wl
+    base = wl.CONFIGS["paged_b128"]
+    md = base.modes[0]
+    m = da.mask(md, base.W, base.B, base.G)
+    lmax = base.prompt[1] + base.n_vis
+    full_pages_per_req = -(-lmax // page_size)
+    budget = base_requests * full_pages_per_req
+    cfg = wl.small_decode("paged_b128", n_seq=max_requests)
+    pos, prompt, seq = wl.positions(cfg)
+    need = np.array([da.ring_pages(m, int(P), lmax, page_size) for P in prompt.tolist()])
+    n = int(np.searchsorted(np.cumsum(need), budget, side="right"))
+    pos, prompt, seq = pos[:n], prompt[:n], seq[:n]
+    bt, total = da.ring_block_table(m, prompt.tolist(), lmax, page_size)
+    assert total <= budget
+    dev = torch.device("cuda:0")
+    kept = sum(da.keep_count(m, int(p), int(P)) for p, P in zip(pos.tolist(), prompt.tolist()))
+    kept_b = kept * kv_bytes_per_key(base)
+    n_copies = max(2, math.ceil(ROTATE_BYTES / kept_b))
+    kc = torch.randn((n_copies * total, base.hkv, page_size, base.hd), dtype=torch.bfloat16, device=dev)
+    vc = torch.randn_like(kc)
+    bts = [(bt + c * total).to(dev).contiguous() for c in range(n_copies)]
+    q = torch.randn((n, base.hq, base.hd), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    pos_d, prompt_d, seq_d = pos.to(dev), prompt.to(dev), seq.to(dev)
+    cap = da.keep_cap(m, int(pos.max()), int(prompt.max()))
+
+    def run(c):
+        da.sparse_decode_attn_masked(m, q, kc, vc, seq_d, pos_d, prompt_d, cap=cap, split=max(cap, 1),
+                                     block_table=bts[c], out=out)
+    burn_in([kc, vc], 0.3)
+    us = graph_us(torch, run, n_copies, steps, warmup)
+    del kc, vc
+    torch.cuda.empty_cache()
+    return {"mode": wl.MODE_NAMES[md], "kv_budget_pages": budget,
+            "kv_budget_GB": round(budget * 2 * base.hkv * page_size * base.hd * 2 / 1e9, 3),
+            "full_cache_requests": base_requests, "ring_requests": n, "ring_pages": total,
+            "kept_MB": round(kept_b / 1e6, 2),
+            "us_per_step": round(us, 2), "tokens_per_s": round(n / (us * 1e-6), 1),
+            "kept_GBps": round(kept_b / (us * 1e-6) / 1e9, 1)}
 
 
 def burn_in(bufs, seconds):
@@ -533,10 +598,14 @@ def burn_in(bufs, seconds):
     return n
 
 
+PROBE_SHAPES = ((2048, 1), (4096, 1), (1024, 2), (512, 4), (256, 8), (2048, 2), (512, 8))
+
+
 def attainable_read(nbytes, steps=50, warmup=10):
     """Streaming-read probe of `nbytes` (rounded down to 16), cold: a HIP
     graph of `steps` reads, each of a different buffer, with >= 1 GiB read
-    between two uses of a buffer.  Returns (microseconds per read, grid)."""
+    between two uses of a buffer; the best over (grid, loads in flight per
+    thread) shapes.  Returns (microseconds per read, (grid, loads))."""
     import torch
     import ar_image_generation_amd as da
     nb = max(2, math.ceil(ROTATE_BYTES / nbytes))
@@ -544,26 +613,12 @@ def attainable_read(nbytes, steps=50, warmup=10):
     bufs = [torch.ones(size // 4, dtype=torch.int32, device="cuda") for _ in range(nb)]
     sink = torch.empty(4096, dtype=torch.int32, device="cuda")
     best = None
-    for grid in (512, 1024, 2048, 4096):
-        for w in range(warmup):
-            da.hbm_read_probe(bufs[w % nb], sink, grid)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for s in range(steps):
-                da.hbm_read_probe(bufs[s % nb], sink, grid)
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
-        del g
+    for grid, depth in PROBE_SHAPES:
+        def run(c, grid=grid, depth=depth):
+            da.hbm_read_probe(bufs[c % nb], sink, grid, loads_in_flight=depth)
+        us = graph_us(torch, run, nb, steps, warmup)
         if best is None or us < best[0]:
-            best = (us, grid)
+            best = (us, (grid, depth))
     del bufs
     torch.cuda.empty_cache()
     return best
@@ -835,7 +890,7 @@ def main():
     achieved = kept / (us_step * 1e-6) / 1e9       # the fused kernel is the whole step
     probe_us, probe_grid = attainable_read(kept, K, W)
     log(f"[bench] attainable: a streaming read of the same {kept / 1e6:.1f} MB takes {probe_us:.2f} us "
-        f"cold ({kept / probe_us / 1e3:.0f} GB/s, grid {probe_grid})")
+        f"cold ({kept / probe_us / 1e3:.0f} GB/s, grid/loads {probe_grid})")
     value = b.n_q / (us_step * 1e-6)
     traffic = traffic_from_profile(cfg.name)
 
@@ -843,7 +898,7 @@ def main():
     per_head = per_head_run(b, K, W) if not args.no_extra else None
     if per_head:
         log(f"[bench] per-head windows {per_head['head_W'][:4]}...: {per_head['us_per_step']:.2f} us, "
-            f"{per_head['kept_MB']:.1f} MB kept, {per_head['kept_GBps']:.0f} GB/s")
+            f"{per_head['read_MB']:.1f} MB read, {per_head['read_GBps']:.0f} GB/s")
 
     # keep-set-aware KV residency: the same step through a ring block table
     residency = {}
@@ -869,6 +924,15 @@ def main():
                 f"fused step {st:.2f} us")
             del rb
             torch.cuda.empty_cache()
+        budget = kv_budget_run(K, W)
+        if cfg.name == "paged_b128":
+            budget["full_cache_us_per_step"] = round(us_step, 2)
+            budget["full_cache_tokens_per_s"] = round(b.n_q / (us_step * 1e-6), 1)
+            budget["tokens_per_s_ratio"] = round(budget["tokens_per_s"] / budget["full_cache_tokens_per_s"], 3)
+        residency["same_kv_budget"] = budget
+        log(f"[bench] same KV budget: {budget['ring_requests']} requests through ring tables vs "
+            f"{budget['full_cache_requests']} on full caches: {budget['us_per_step']:.2f} us/step, "
+            f"{budget['tokens_per_s']:.0f} tokens/s")
 
     # the headline workload's other sparse mode(s)
     other_modes = {}
@@ -953,8 +1017,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic},
-        "attainable": {"what": "streaming-read probe of the kept byte count, cold, best grid",
-                       "bytes": kept, "us": round(probe_us, 3),
+        "attainable": {"what": "streaming-read probe (nontemporal 16-byte loads) of the kept byte "
+                               "count, cold, best (grid, loads in flight) shape",
+                       "bytes": kept, "us": round(probe_us, 3), "grid_loads": list(probe_grid),
                        "GBps": round(kept / probe_us / 1e3, 1),
                        "frac_of_peak": round(kept / probe_us / 1e3 / HBM_PEAK_GBPS, 4),
                        "step_frac_of_attainable": round(probe_us / us_step, 4)},

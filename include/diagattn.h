@@ -391,13 +391,15 @@ int da_band_prefill_attn(const da_mask* m /* [host] */, da_dtype dtype, int32_t 
                          void* stream);
 
 /* Measurement: streaming read of `bytes` bytes at `buf` (16-byte aligned, a
- * multiple of 16) by `grid` workgroups of 256 threads, 16-byte loads, eight
- * in flight per thread; writes one word per workgroup to sink[grid].  Its
- * bytes / duration is the attainable HBM read bandwidth that decode's
- * kept-byte bandwidth is compared with.  Errors: DA_EINVAL for NULL
- * pointers, a bad size or alignment, grid < 1. */
+ * multiple of 16) by `grid` workgroups of 256 threads, 16-byte nontemporal
+ * loads, `loads_in_flight` (1, 2, 4, 8 or 16) independent loads per thread
+ * per iteration; writes one word per workgroup to sink[grid].  Its bytes /
+ * duration, best over grids and depths, is the attainable HBM read
+ * bandwidth that decode's kept-byte bandwidth is compared with.  Errors:
+ * DA_EINVAL for NULL pointers, a bad size or alignment, grid < 1, or
+ * another loads_in_flight. */
 int da_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid,
-                      void* stream);
+                      int32_t loads_in_flight, void* stream);
 
 #ifdef __cplusplus
 }

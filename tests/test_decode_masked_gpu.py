@@ -209,6 +209,9 @@ def test_kv_append(name, n_seq, split):
         assert torch.equal(got.cpu(), ref.cpu()), mode
         assert torch.equal(got_lse.cpu(), ref_lse.cpu()), mode
         assert torch.equal(k_miss, k_full) and torch.equal(v_miss, v_full), mode
+        # and against the oracle on the logical cache (contiguous and paged)
+        ref_o, ref_l = run_oracle(inp, mode)
+        assert_close(got.cpu(), got_lse.cpu(), ref_o, ref_l, cfg.dtype)
 
 
 @pytest.mark.parametrize("split", [37, 4096])

@@ -1,12 +1,13 @@
 """Decode through the ring block table (rows older than the live window
-recycled) returns exactly what it returns on the full cache."""
+recycled) returns exactly what it returns on the full cache, and matches
+the oracle run on the logical (full) cache."""
 import pytest
 import torch
 
 import ar_image_generation_amd as da
 import oracle as O
 import workloads as wl
-from gpu_helpers import dev
+from gpu_helpers import assert_close, dev, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -57,3 +58,7 @@ def test_ring_cache_decode_equals_full_cache(name, n_seq):
         assert torch.equal(got.cpu(), ref.cpu()), mode
         assert torch.equal(got_lse.cpu(), ref_lse.cpu()), mode
         assert torch.equal(got2.cpu(), ref.cpu()), mode
+        # and against the oracle on the logical cache: the ring holds every
+        # row the keep-sets read
+        ref_o, ref_l = run_oracle(inp, mode)
+        assert_close(got.cpu(), got_lse.cpu(), ref_o, ref_l, cfg.dtype)
