@@ -37,6 +37,7 @@
 #include "common.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace da {
 
@@ -831,42 +832,49 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
   // (positions follow the offsets: the table holds min(split, cap) rows)
   int32_t* rowpos = reinterpret_cast<int32_t*>(rowoff + (split_p < cap_p ? split_p : cap_p));
   {
-    constexpr int IPT = 4;
+    // IPT rows a thread a round; only as many rows as the chunk has are
+    // computed (a closed-form entry costs an integer division)
     const int32_t* myidx = MASKED ? nullptr : m1_p + (int64_t)qi * cap_p + r0;
-    for (int base = 0; base < nrows; base += IPT * 256) {
-      int jj[IPT];
+    auto fill = [&](auto ipt) {
+      constexpr int IPT = decltype(ipt)::value;
+      for (int base = 0; base < nrows; base += IPT * 256) {
+        int jj[IPT];
 #pragma unroll
-      for (int u = 0; u < IPT; ++u) {
-        const int r = base + u * 256 + t;
-        const int rc = r < nrows ? r : nrows - 1;
-        int j;
-        if constexpr (MASKED) j = kc.entry(r0 + rc);
-        else j = myidx[rc];
-        jj[u] = clampi(j, 0, a.max_len - 1);
-        if constexpr (PERHEAD) {
-          if (r < nrows) rowpos[r] = j;
+        for (int u = 0; u < IPT; ++u) {
+          const int r = base + u * 256 + t;
+          const int rc = r < nrows ? r : nrows - 1;
+          int j;
+          if constexpr (MASKED) j = kc.entry(r0 + rc);
+          else j = myidx[rc];
+          jj[u] = clampi(j, 0, a.max_len - 1);
+          if constexpr (PERHEAD) {
+            if (r < nrows) rowpos[r] = j;
+          }
+          if (lists_out && r < nrows) my_out[r] = j;
         }
-        if (lists_out && r < nrows) my_out[r] = j;
+        int64_t o[IPT];
+        if (bt) {
+          int pg[IPT];
+#pragma unroll
+          for (int u = 0; u < IPT; ++u) pg[u] = bt[jj[u] >> a.ps_shift];
+#pragma unroll
+          for (int u = 0; u < IPT; ++u)
+            o[u] = (int64_t)clampi(pg[u], 0, a.n_pages - 1) * a.page_stride +
+                   (int64_t)(jj[u] & a.ps_mask) * a.slot_stride;
+        } else {
+#pragma unroll
+          for (int u = 0; u < IPT; ++u) o[u] = (int64_t)sq * a.page_stride + (int64_t)jj[u] * a.slot_stride;
+        }
+#pragma unroll
+        for (int u = 0; u < IPT; ++u) {
+          const int r = base + u * 256 + t;
+          if (r < nrows) rowoff[r] = o[u];
+        }
       }
-      int64_t o[IPT];
-      if (bt) {
-        int pg[IPT];
-#pragma unroll
-        for (int u = 0; u < IPT; ++u) pg[u] = bt[jj[u] >> a.ps_shift];
-#pragma unroll
-        for (int u = 0; u < IPT; ++u)
-          o[u] = (int64_t)clampi(pg[u], 0, a.n_pages - 1) * a.page_stride +
-                 (int64_t)(jj[u] & a.ps_mask) * a.slot_stride;
-      } else {
-#pragma unroll
-        for (int u = 0; u < IPT; ++u) o[u] = (int64_t)sq * a.page_stride + (int64_t)jj[u] * a.slot_stride;
-      }
-#pragma unroll
-      for (int u = 0; u < IPT; ++u) {
-        const int r = base + u * 256 + t;
-        if (r < nrows) rowoff[r] = o[u];
-      }
-    }
+    };
+    if (nrows <= 256) fill(std::integral_constant<int, 1>{});
+    else if (nrows <= 512) fill(std::integral_constant<int, 2>{});
+    else fill(std::integral_constant<int, 4>{});
   }
   __syncthreads();
   if constexpr (MASKED) {

@@ -655,6 +655,11 @@ def profile_run(args):
     log(f"[bench] profile run: {us:.2f} us/step; probe {PROBE_BYTES} bytes")
 
 
+def is_decode_kernel(name):
+    """The decode step's kernel: the vector form or the matrix-core form."""
+    return "decode_kernel" in name or "decode_mfma_kernel" in name
+
+
 def summarize(args):
     """Writes profiles/decode_<workload>.txt from three rocprofv3 runs of
     `bench.py --profile-run`: --kernel-trace, --pmc FETCH_SIZE, --pmc WRITE_SIZE."""
@@ -672,7 +677,7 @@ def summarize(args):
         return out
 
     def decode_rows(rs):
-        return [r for r in rs if "decode_kernel" in r.get("Kernel_Name", "")]
+        return [r for r in rs if is_decode_kernel(r.get("Kernel_Name", ""))]
 
     tr = decode_rows(rows(trace_dir, "kernel_trace.csv"))
     durs = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr)
@@ -687,7 +692,7 @@ def summarize(args):
                 continue
             per.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), 0.0)
             per[(r["Kernel_Name"], r["Dispatch_Id"])] += float(r["Counter_Value"])
-        dec = [v for (k, _), v in per.items() if "decode_kernel" in k]
+        dec = [v for (k, _), v in per.items() if is_decode_kernel(k)]
         probe = [v for (k, _), v in per.items() if "read_probe_kernel" in k]
         # the probe buffer's fill: a plain write kernel of PROBE_BYTES
         fill = [v for (k, _), v in per.items() if "FillFunctor<int>" in k]
@@ -710,10 +715,10 @@ def summarize(args):
         f"# rocprofv3 summary: decode kernel of the benchmark step (keep-set computed in the "
         f"kernel, lists written, attention), workload {cfg.name}",
         "# commands (repo root, TMPDIR=/tmp):",
-        f"#   rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o run -- python3 bench.py --profile-run --steps {args.steps} --warmup {args.warmup}",
-        f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o run -- python3 bench.py --profile-run --steps {args.steps} --warmup {args.warmup}",
-        f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o run -- python3 bench.py --profile-run --steps {args.steps} --warmup {args.warmup}",
-        f"#   python3 bench.py --summarize {trace_dir} {fetch_dir} {write_dir}",
+        f"#   rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o run -- python3 bench.py --profile-run --workload {cfg.name} --steps {args.steps} --warmup {args.warmup}",
+        f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o run -- python3 bench.py --profile-run --workload {cfg.name} --steps {args.steps} --warmup {args.warmup}",
+        f"#   rocprofv3 --pmc WRITE_SIZE -f csv -d {write_dir} -o run -- python3 bench.py --profile-run --workload {cfg.name} --steps {args.steps} --warmup {args.warmup}",
+        f"#   python3 bench.py --summarize {trace_dir} {fetch_dir} {write_dir} --workload {cfg.name}",
         f"kernel = {kname}",
         f"dispatches = {len(durs)}",
         f"avg_duration_us = {avg / 1e3:.3f}",
@@ -742,11 +747,11 @@ def summarize(args):
     slines = [
         f"# rocprofv3 --kernel-trace --stats summary: benchmark step (keep-set build, lists and "
         f"attention in one launch), workload {cfg.name}",
-        f"# ({cfg.n_seq} requests x {cfg.hq} heads, head_dim {cfg.hd}, {cfg.dtype}, P={cfg.prompt[0]}, "
+        f"# ({cfg.n_seq} requests x {cfg.hq}/{cfg.hkv} heads, head_dim {cfg.hd}, {cfg.dtype}, P={cfg.prompt}, "
         f"{cfg.G}x{cfg.G} grid, W={cfg.W}, B={cfg.B}, {wl.MODE_NAMES[cfg.modes[0]]}; cold cache copies)",
         "# command (repo root, TMPDIR=/tmp):",
         f"#   rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o run -- python3 bench.py "
-        f"--profile-run --steps {args.steps} --warmup {args.warmup}",
+        f"--profile-run --workload {cfg.name} --steps {args.steps} --warmup {args.warmup}",
         "# columns: name | calls | avg_ns | min_ns | max_ns   (library kernels only)",
     ] + [f"{r['Name']} | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | {r['MaxNs']}"
          for r in stats]
