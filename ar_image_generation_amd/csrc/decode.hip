@@ -694,7 +694,7 @@ __global__ void __launch_bounds__(256) decode_kernel(const int32_t* m0_p, const 
 // entries in the same order as decode_kernel reads.  The four waves' states
 // meet in LDS at the end, as in decode_kernel, whose output and partial
 // formats are kept (the merge kernel serves both).
-template <int HD, int GRP, int FORM>
+template <int HD, int GRP, int FORM, bool APPEND>
 __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, const int32_t* m1_p,
                                                           const int32_t* seq_p, int hkv_p,
                                                           int max_split_p, int cap_p, int split_p,
@@ -788,7 +788,8 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
     }
   };
   if constexpr (MASKED) {
-    appending = a.k_new != nullptr;
+    // KV append: a kernel of its own (the code, unused, cost a step ~1 us)
+    appending = APPEND && a.k_new != nullptr;
     if (appending && t < 2 * CPR) {
       const void* src = t < CPR ? a.k_new : a.v_new;
       const int64_t off = ((int64_t)qi * a.hkv + g) * HD + (t % CPR) * 8;
@@ -1170,13 +1171,19 @@ static decode_fn pick_grp(int grp, int np) {
 }
 
 // Matrix-core kernel for bf16 groups of 2, 4 or 8 query heads a kv head.
-template <int FORM>
-static decode_fn pick_mfma(int head_dim, int grp) {
+template <int FORM, bool APPEND>
+static decode_fn pick_mfma_a(int head_dim, int grp) {
   if (head_dim == 64)
-    return grp == 2 ? decode_mfma_kernel<64, 2, FORM>
-                    : grp == 4 ? decode_mfma_kernel<64, 4, FORM> : decode_mfma_kernel<64, 8, FORM>;
-  return grp == 2 ? decode_mfma_kernel<128, 2, FORM>
-                  : grp == 4 ? decode_mfma_kernel<128, 4, FORM> : decode_mfma_kernel<128, 8, FORM>;
+    return grp == 2 ? decode_mfma_kernel<64, 2, FORM, APPEND>
+                    : grp == 4 ? decode_mfma_kernel<64, 4, FORM, APPEND> : decode_mfma_kernel<64, 8, FORM, APPEND>;
+  return grp == 2 ? decode_mfma_kernel<128, 2, FORM, APPEND>
+                  : grp == 4 ? decode_mfma_kernel<128, 4, FORM, APPEND> : decode_mfma_kernel<128, 8, FORM, APPEND>;
+}
+
+template <int FORM>
+static decode_fn pick_mfma(int head_dim, int grp, bool append) {
+  if constexpr (FORM == 0) return pick_mfma_a<0, false>(head_dim, grp);
+  else return append ? pick_mfma_a<FORM, true>(head_dim, grp) : pick_mfma_a<FORM, false>(head_dim, grp);
 }
 
 static bool use_mfma(da_dtype dtype, int grp) { return dtype == DA_BF16 && grp >= 2; }
@@ -1339,7 +1346,7 @@ static int launch_decode(const DecodeArgs& a, da_dtype dtype, int head_dim, void
   if (use_mfma(dtype, grp)) {
     // row table in LDS: offsets, and positions for per-head masks
     lds = (size_t)chunk * (sizeof(int64_t) + (FORM == 2 ? sizeof(int32_t) : 0));
-    dk = pick_mfma<FORM>(head_dim, grp);
+    dk = pick_mfma<FORM>(head_dim, grp, a.k_new != nullptr);
   } else {
     // row offsets in LDS: every list, and the mask form of a paged cache
     lds = FORM >= 1 && !a.block_table ? 0 : (size_t)chunk * sizeof(int64_t);
