@@ -95,15 +95,18 @@ __device__ inline float sum_over_row_groups(float x) {
 }
 
 // LDS position of 16-byte chunk p of row r is p ^ swz(r) in row-major tiles
-// of CPR chunks a row.  With 16 chunks (head_dim 128), under a model of 64
-// four-byte banks, swz spreads both read patterns over all banks: rows read
-// one chunk each (16 consecutive rows, one chunk: swz is a permutation of
-// 0..15) and the transposing reads (8 consecutive rows, two adjacent chunks
-// 2m, 2m+1: swz takes distinct values >> 1 on each aligned 8 rows and keeps
-// bit 0 fixed).  With 8 chunks (head_dim 64) it is r % 8.
+// of CPR chunks a row.  The tiles are read two ways: as matrix-core A
+// operands (ds_read_b128: lane l reads row l % 16, chunk 4c + l / 16) and
+// transposed (ds_read_b64_tr_b16: rows 4(l / 16) + (l % 16) / 4, chunks
+// 2m + (l % 4) / 2).  Both patterns read with no bank conflict under these
+// swizzles, as measured with the LDS bank-conflict counter on this part
+// (the earlier choice for 16 chunks, ((r & 7) << 1) | ((r >> 3) & 1), left
+// four conflict cycles on every operand read).  The 16-chunk swizzle is an
+// XOR-linear map of r mod 16, so rows 16 apart share it and their LDS
+// addresses differ by a constant.
 template <int CPR>
 __device__ inline int swz(int r) {
-  if constexpr (CPR == 16) return ((r & 7) << 1) | ((r >> 3) & 1);
+  if constexpr (CPR == 16) return (r & 3) ^ ((r & 1) << 2) ^ ((r & 4) << 1) ^ (((r >> 3) & 1) * 9);
   else return r % CPR;
 }
 

@@ -631,20 +631,30 @@ def profile_run(args):
     band prefill instead."""
     import torch
     import workloads as wl
-    import ar_image_generation_amd as da
     if args.prefill:
         pb = PrefillBench(wl.PREFILL_CONFIGS["prefill_b2"], n_copies=2)
         pb.burn(0.5)
         us = pb.time_graph(pb.cfg.mode, args.steps, args.warmup)
+        del pb
+        torch.cuda.empty_cache()
+        counter_calibration()
         log(f"[bench] prefill profile run: {us:.2f} us per launch")
         return
     cfg = wl.CONFIGS[args.workload]
     b = DecodeBench(cfg, split=args.split)
     burn_in([b.k, b.v], 0.5)
     us = b.time_graph(cfg.modes[0], args.steps, args.warmup, path="fused")
-    # counter calibration: a streaming read of PROBE_BYTES that are not in
-    # any cache -- written, then pushed out of the L2s and the Infinity
-    # Cache by writing as many other bytes -- read once
+    counter_calibration()
+    log(f"[bench] profile run: {us:.2f} us/step; probe {PROBE_BYTES} bytes")
+
+
+def counter_calibration():
+    """Kernels of known traffic for scaling the memory counters: a fill of
+    PROBE_BYTES, then a streaming read of PROBE_BYTES that are in no cache
+    -- written, then pushed out of the L2s and the Infinity Cache by writing
+    as many other bytes -- read once."""
+    import torch
+    import ar_image_generation_amd as da
     buf = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
     evict = torch.ones(PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
@@ -652,7 +662,6 @@ def profile_run(args):
     sink = torch.empty(4096, dtype=torch.int32, device="cuda")
     da.hbm_read_probe(buf, sink, 2048)
     torch.cuda.synchronize()
-    log(f"[bench] profile run: {us:.2f} us/step; probe {PROBE_BYTES} bytes")
 
 
 def is_decode_kernel(name):
@@ -759,16 +768,24 @@ def summarize(args):
         "\n".join(slines) + "\n")
 
 
+def is_prefill_kernel(name):
+    """The band prefill's attention kernel: the tile form or the slab form."""
+    return "prefill_kernel" in name or "prefill_slab_kernel" in name
+
+
 def summarize_prefill(args):
     """Writes profiles/prefill_<workload>.txt from rocprofv3 runs of
-    `bench.py --profile-run --prefill`: --kernel-trace, and two --pmc runs
-    (matrix-core busy cycles with GRBM_GUI_ACTIVE; instruction mix)."""
+    `bench.py --profile-run --prefill`: a --kernel-trace folder, then --pmc
+    folders (matrix-core busy cycles with GRBM_GUI_ACTIVE, instruction mix,
+    the LDS bank-conflict counter on its own, FETCH_SIZE, WRITE_SIZE).
+    FETCH_SIZE and WRITE_SIZE are scaled by what they read for the cold
+    streaming read and the fill of PROBE_BYTES in the same run."""
     import csv
     import glob
     import workloads as wl
     import ar_image_generation_amd as da
     cfg = wl.PREFILL_CONFIGS["prefill_b2"]
-    trace_dir, busy_dir, mix_dir = args.summarize
+    trace_dir, pmc_dirs = args.summarize[0], args.summarize[1:]
 
     def rows(d, suffix):
         out = []
@@ -776,14 +793,14 @@ def summarize_prefill(args):
             out += list(csv.DictReader(open(f)))
         return out
 
-    tr = [r for r in rows(trace_dir, "kernel_trace.csv") if "prefill_kernel" in r["Kernel_Name"]]
+    tr = [r for r in rows(trace_dir, "kernel_trace.csv") if is_prefill_kernel(r["Kernel_Name"])]
     durs = sorted(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in tr)
     avg = sum(durs) / len(durs) if durs else float("nan")
 
-    def per_dispatch(d):
+    def per_dispatch(d, match):
         acc = {}
         for r in rows(d, "counter_collection.csv"):
-            if "prefill_kernel" not in r["Kernel_Name"]:
+            if not match(r["Kernel_Name"]):
                 continue
             key = (r["Dispatch_Id"], r["Counter_Name"])
             acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
@@ -792,26 +809,59 @@ def summarize_prefill(args):
         return {nm: sum(acc[(dd, nm)] for dd in disp if (dd, nm) in acc) / max(1, len(disp))
                 for nm in names}
 
-    busy = per_dispatch(busy_dir)
-    mix = per_dispatch(mix_dir)
+    counters, dirs_of = {}, {}
+    for d in pmc_dirs:
+        for k, v in per_dispatch(d, is_prefill_kernel).items():
+            counters[k] = v
+            dirs_of[k] = d
+    probe = {}
+    for d in pmc_dirs:
+        probe.update(per_dispatch(d, lambda k: "read_probe_kernel" in k))
+    # the probe buffer's fill: the largest int32 fill kernel of the run
+    fill = {}
+    for d in pmc_dirs:
+        for r in rows(d, "counter_collection.csv"):
+            if "FillFunctor<int>" in r["Kernel_Name"]:
+                nm = r["Counter_Name"]
+                acc = fill.setdefault(nm, {})
+                acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    fill = {nm: max(v.values()) for nm, v in fill.items()}
     n_xcd, n_simd = 8, 1024
     util = None
-    if busy.get("GRBM_GUI_ACTIVE") and busy.get("SQ_VALU_MFMA_BUSY_CYCLES"):
-        cycles = busy["GRBM_GUI_ACTIVE"] / n_xcd          # per-XCD counter, summed over XCDs
-        util = busy["SQ_VALU_MFMA_BUSY_CYCLES"] / (n_simd * cycles)
+    if counters.get("GRBM_GUI_ACTIVE") and counters.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+        cycles = counters["GRBM_GUI_ACTIVE"] / n_xcd          # per-XCD counter, summed over XCDs
+        util = counters["SQ_VALU_MFMA_BUSY_CYCLES"] / (n_simd * cycles)
     m = da.mask(cfg.mode, cfg.W, cfg.B, cfg.G)
     kept = sum(da.keep_count(m, i, cfg.P) for i in range(cfg.n)) * cfg.batch * cfg.heads
     flops = 4.0 * cfg.hd * kept
     bytes_ = 4 * cfg.batch * cfg.heads * cfg.n * cfg.hd * 2
+    extra = []
+    if counters.get("SQ_INSTS_MFMA"):
+        # v_mfma_f32_16x16x32_bf16: 16 * 16 * 32 multiply-adds
+        executed = counters["SQ_INSTS_MFMA"] * 2 * 16 * 16 * 32
+        extra.append(f"executed_mfma_GFLOP = {executed / 1e9:.3f} ({executed / flops:.2f} x algorithmic)")
+    if counters.get("FETCH_SIZE") and probe.get("FETCH_SIZE"):
+        fscale = (PROBE_BYTES / 1024.0) / probe["FETCH_SIZE"]
+        extra.append(f"fetch_scale = {fscale:.4f} (cold read of {PROBE_BYTES} bytes)")
+        hbm = counters["FETCH_SIZE"] * fscale * 1024
+        if counters.get("WRITE_SIZE") and fill.get("WRITE_SIZE"):
+            wscale = (PROBE_BYTES / 1024.0) / fill["WRITE_SIZE"]
+            extra.append(f"write_scale = {wscale:.4f} (fill of {PROBE_BYTES} bytes)")
+            hbm += counters["WRITE_SIZE"] * wscale * 1024
+        extra.append(f"hbm_bytes_per_launch = {hbm:.6g} ({hbm / bytes_:.3f} x Q, K, V, O once)")
+    cmd = f"python3 bench.py --profile-run --prefill --steps {args.steps} --warmup {args.warmup}"
     lines = [
         f"# rocprofv3 summary: band prefill kernel, workload {cfg.name}",
         f"# (batch {cfg.batch} x {cfg.heads} heads x {cfg.n} tokens, head_dim {cfg.hd}, bf16; causal and "
         f"prompt {cfg.P} + row-diagonal W={cfg.W} B={cfg.B} G={cfg.G})",
         "# commands (repo root, TMPDIR=/tmp):",
-        f"#   rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o run -- python3 bench.py --profile-run --prefill --steps {args.steps} --warmup {args.warmup}",
-        f"#   rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_BUSY_CYCLES GRBM_GUI_ACTIVE -f csv -d {busy_dir} -o run -- python3 bench.py --profile-run --prefill --steps {args.steps} --warmup {args.warmup}",
-        f"#   rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_LDS SQ_WAVES -f csv -d {mix_dir} -o run -- python3 bench.py --profile-run --prefill --steps {args.steps} --warmup {args.warmup}",
-        f"#   python3 bench.py --summarize {trace_dir} {busy_dir} {mix_dir} --prefill",
+        f"#   rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o run -- {cmd}",
+    ]
+    for d in pmc_dirs:
+        names = " ".join(sorted(k for k in counters if dirs_of[k] == d))
+        lines.append(f"#   rocprofv3 --pmc {names} -f csv -d {d} -o run -- {cmd}")
+    lines += [
+        f"#   python3 bench.py --summarize {trace_dir} {' '.join(pmc_dirs)} --prefill",
         "# mfma_utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs)",
         f"kernel = {tr[0]['Kernel_Name'] if tr else '?'}",
         f"dispatches = {len(durs)}",
@@ -821,7 +871,7 @@ def summarize_prefill(args):
         f"achieved_TFLOPs_from_avg = {flops / avg / 1e3 if durs else float('nan'):.2f}",
         f"hbm_bytes_QKVO = {bytes_}",
         f"mfma_utilisation = {util}",
-    ] + [f"{k} = {v:.6g}" for k, v in sorted(busy.items())] + [f"{k} = {v:.6g}" for k, v in sorted(mix.items())]
+    ] + extra + [f"{k} = {v:.6g}" for k, v in sorted(counters.items())]
     out = os.path.join(ROOT, "profiles", f"prefill_{cfg.name}.txt")
     open(out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -841,12 +891,15 @@ def main():
                     help="run only the timed decode launches and one probe (for rocprofv3)")
     ap.add_argument("--prefill", action="store_true",
                     help="with --profile-run / --summarize: the band prefill kernel")
-    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="write the profiles/ summary from three rocprofv3 output folders")
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
+                    help="write the profiles/ summary from rocprofv3 output folders: decode "
+                         "TRACE_DIR FETCH_DIR WRITE_DIR; with --prefill TRACE_DIR PMC_DIR...")
     args = ap.parse_args()
     if args.summarize:
         if args.prefill:
             summarize_prefill(args)
+        elif len(args.summarize) != 3:
+            ap.error("decode --summarize takes TRACE_DIR FETCH_DIR WRITE_DIR")
         else:
             summarize(args)
         return

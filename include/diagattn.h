@@ -359,7 +359,11 @@ int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t
  * whole sequence is attended at once.  Only the key tiles listed in `tiles`
  * (da_prefill_tiles_build with the same mask, n and prompt_len) are
  * computed; element masks (a 64-bit keep word per row and key tile) are
- * applied where a wave's blocks are not all entirely kept.
+ * applied where a wave's blocks are not all entirely kept.  Row-diagonal
+ * masks with B <= 8, 2B + 1 < G and G a multiple of 16 take a band-shaped
+ * form instead: the prompt keys in 64-key tiles and, per 16-row block and
+ * raster-row diagonal k, only the 32 keys around i - kG; that form does not
+ * read `tiles` (it must still be given, of the size below).
  *
  *   q, out [batch][heads][n][head_dim], k, v [batch][kv_heads][n][head_dim],
  *          bf16, head_dim elements contiguous and 16-byte aligned;
@@ -379,7 +383,8 @@ int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t
  * n <= 65536 tokens; in ROWDIAG mode G <= 1024; the k and v position strides
  * such that 63 positions plus one row span under 4 GiB (32-bit offsets
  * within a 64-key tile).
- * Errors: DA_EINVAL (mask, null pointers, sizes, strides, alignment),
+ * Errors: DA_EINVAL (mask, null pointers, sizes, strides, alignment, a
+ * scale that is not positive and finite),
  * DA_ENOTSUP (causal = 0, dtype other than bf16, head_dim not 64/128,
  * n > 65536, ROWDIAG with G > 1024, k/v position stride too large),
  * DA_ECAPACITY (tiles_bytes below da_prefill_tiles_bytes(batch, n)). */

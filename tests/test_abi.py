@@ -154,6 +154,11 @@ def test_prefill_limits_are_reported_before_launch():
     assert lib.da_band_prefill_attn(rd, 1, 1, 2, 2, 1024, 128, dummy, dummy, dummy, dummy, strides,
                                     dummy, dummy, need - 1, 0.1, None, None) == -3
     assert "tiles buffer" in _native.last_error()
+    # the scale must be positive and finite (masked scores are -inf before it)
+    for bad in (0.0, -0.5, float("inf"), float("nan")):
+        assert lib.da_band_prefill_attn(rd, 1, 1, 2, 2, 1024, 128, dummy, dummy, dummy, dummy, strides,
+                                        dummy, dummy, 1 << 30, bad, None, None) == -1
+        assert "scale" in _native.last_error()
 
 
 def test_decode_workspace_size():

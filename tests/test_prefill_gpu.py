@@ -145,6 +145,25 @@ def test_random_masks_and_shapes(seed):
     check(out, lse, oracle_rows(q, k, v, prompt, mode, W, B, G, rows))
 
 
+@pytest.mark.parametrize("n,P,W,B,G,hd", [(300, 17, 96, 2, 32, 128), (300, 0, 96, 8, 48, 128),
+                                          (129, 5, 40, 8, 32, 64), (500, 64, 144, 2, 48, 128),
+                                          (77, 100, 30, 0, 16, 64), (513, 3, 1000, 7, 16, 128),
+                                          (1, 0, 4, 1, 16, 128), (1100, 256, 256, 3, 64, 128),
+                                          (260, 260, 64, 3, 32, 64), (700, 31, 2**31 - 1, 8, 64, 128),
+                                          (1030, 0, 160, 5, 80, 128)])
+def test_row_diagonal_slab_shapes(n, P, W, B, G, hd):
+    """Row-diagonal masks whose bands fit 32-key slabs (B <= 8, 2B + 1 < G,
+    G a multiple of 16): ragged lengths, prompts longer than the sequence,
+    windows past the sequence, the widest band, a group of query heads per
+    kv head.  Every row against the oracle."""
+    q = randn((2, 4, n, hd), 31)
+    k, v = randn((2, 2, n, hd), 32), randn((2, 2, n, hd), 33)
+    prompt = [P, n // 3]
+    out, lse = run(q, k, v, prompt, O.ROWDIAG, W, B, G)
+    rows = [(b, h, i) for b in range(2) for h in range(4) for i in range(n)]
+    check(out, lse, oracle_rows(q, k, v, prompt, O.ROWDIAG, min(W, n), B, G, rows))
+
+
 @pytest.mark.parametrize("mode", [O.ROWDIAG, O.DENSE])
 def test_longest_sequence_sampled_rows(mode):
     """The longest sequence the prefill takes (65536 tokens, its whole tile
@@ -159,3 +178,27 @@ def test_longest_sequence_sampled_rows(mode):
     pick = {0, 1, 127, 128, 255, 256, 257, n - 129, n - 128, n - 2, n - 1}
     pick |= {int(x) for x in rng.integers(0, n, 16)}
     check(out, lse, oracle_rows(q, k, v, [P], mode, W, B, G, [(0, 0, i) for i in sorted(pick)]))
+
+
+@pytest.mark.parametrize("W,B,G", [(2**31 - 1, 2**31 - 1, 1), (2**31 - 1, 2**31 - 1, 7),
+                                   (40, 2**31 - 1, 5), (2**31 - 1, 2**30, 9),
+                                   (2**31 - 1, 3, 9), (100, 2**30, 64)])
+def test_window_and_band_at_the_int32_limit(W, B, G):
+    """W and B up to INT32_MAX: a window or band wider than the sequence
+    keeps what an unbounded one keeps, with no overflow in the band
+    pattern or the range tests (rows with P = 0 and with a prompt)."""
+    n = 150
+    q, k, v = randn((2, 2, n, 128), 21), randn((2, 2, n, 128), 22), randn((2, 2, n, 128), 23)
+    prompt = [0, 17]
+    # The oracle's vectorised rows loop over the diagonals a window can
+    # reach, so it is run with W, B cut to n; the pairwise definition
+    # (O.keep, no such loop) confirms the cut changes no pair.
+    Wr, Br = min(W, n), min(B, n)
+    for mode in (O.ROWDIAG, O.BAND):
+        for P in prompt:
+            for i in range(0, n, 7):
+                want = [O.keep(i, j, P=P, W=W, B=B, G=G, mode=mode) for j in range(n)]
+                assert O.keep_row(i, n, P=P, W=Wr, B=Br, G=G, mode=mode).tolist() == want
+        out, lse = run(q, k, v, prompt, mode, W, B, G)
+        rows = [(b, h, i) for b in range(2) for h in range(2) for i in range(n)]
+        check(out, lse, oracle_rows(q, k, v, prompt, mode, Wr, Br, G, rows))
