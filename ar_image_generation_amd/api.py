@@ -60,45 +60,58 @@ def keep_cap(m: DaMask, max_pos: int, max_prompt: int, n_keys: int = 0, head_wb=
 
 def keepset_build(m: DaMask, pos: torch.Tensor, prompt_len: torch.Tensor, cap: int,
                   n_keys: int = 0, max_runs: int = 0, count=None, idx=None,
-                  n_runs=None, runs=None):
+                  n_runs=None, runs=None, head_wb=None):
     """Returns (count [n_q], idx [n_q, cap], n_runs [n_q] or None,
-    runs [n_q, max_runs, 2] or None), all int32 on pos.device."""
+    runs [n_q, max_runs, 2] or None), all int32 on pos.device.  With
+    ``head_wb`` (device int32 [n_heads, 2] (W, B) per head) one list per
+    (query, head): count [n_q, n_heads], idx [n_q, n_heads, cap], ..."""
     return _keepset_build(m, pos, prompt_len, cap, n_keys, max_runs, count, idx, n_runs, runs,
-                          0, 0, None, None)[:4]
+                          0, 0, None, None, head_wb)[:4]
 
 
 def keepset_tiles(m: DaMask, pos: torch.Tensor, prompt_len: torch.Tensor, cap: int, tile: int,
-                  cap_tiles: int, n_keys: int = 0, tiles=None, n_tiles=None):
+                  cap_tiles: int, n_keys: int = 0, tiles=None, n_tiles=None, head_wb=None):
     """keepset_build with the split-KV tile list: returns (count, idx,
-    tiles [cap_tiles, 2] int32 (query, first entry), n_tiles [1] int64)."""
+    tiles [cap_tiles, 2] int32 (list, first entry), n_tiles [1] int64); a
+    list is a query, or with ``head_wb`` a (query, head) pair q*n_heads + h."""
     if tile < 1:
         raise ValueError("keepset_tiles: tile must be >= 1")
     count, idx, _, _, tiles, n_tiles = _keepset_build(m, pos, prompt_len, cap, n_keys, 0, None,
                                                       None, None, None, tile, cap_tiles, tiles,
-                                                      n_tiles)
+                                                      n_tiles, head_wb)
     return count, idx, tiles, n_tiles
 
 
 def _keepset_build(m, pos, prompt_len, cap, n_keys, max_runs, count, idx, n_runs, runs,
-                   tile, cap_tiles, tiles, n_tiles):
+                   tile, cap_tiles, tiles, n_tiles, head_wb=None):
     _need_cuda("keepset_build", pos, prompt_len)
     n_q = pos.numel()
     dev = pos.device
+    if head_wb is not None:
+        if head_wb.dtype != torch.int32 or not head_wb.is_contiguous() or head_wb.dim() != 2 or \
+                head_wb.shape[1] != 2 or head_wb.shape[0] < 1 or head_wb.device != dev:
+            raise ValueError("keepset_build: head_wb must be a contiguous int32 [n_heads, 2] tensor "
+                             "on the device of pos")
+        nh, lead = head_wb.shape[0], (n_q, head_wb.shape[0])
+    else:
+        nh, lead = 1, (n_q,)
     if count is None:
-        count = torch.empty(n_q, dtype=torch.int32, device=dev)
+        count = torch.empty(lead, dtype=torch.int32, device=dev)
     if idx is None:
-        idx = torch.empty((n_q, cap), dtype=torch.int32, device=dev)
+        idx = torch.empty(lead + (cap,), dtype=torch.int32, device=dev)
     if max_runs > 0:
         if n_runs is None:
-            n_runs = torch.empty(n_q, dtype=torch.int32, device=dev)
+            n_runs = torch.empty(lead, dtype=torch.int32, device=dev)
         if runs is None:
-            runs = torch.empty((n_q, max_runs, 2), dtype=torch.int32, device=dev)
+            runs = torch.empty(lead + (max_runs, 2), dtype=torch.int32, device=dev)
     for t in (pos, prompt_len, count, idx, n_runs, runs, tiles):
         if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
             raise ValueError("keepset_build: int32 contiguous tensors expected")
-    if pos.numel() != n_q or prompt_len.numel() != n_q or count.numel() < n_q or \
-            idx.numel() < n_q * cap:
-        raise ValueError("keepset_build: pos, prompt_len, count [n_q] and idx [n_q, cap] expected")
+    if pos.numel() != n_q or prompt_len.numel() != n_q or count.numel() < n_q * nh or \
+            idx.numel() < n_q * nh * cap or \
+            (n_runs is not None and (n_runs.numel() < n_q * nh or runs.numel() < n_q * nh * max_runs * 2)):
+        raise ValueError("keepset_build: pos, prompt_len [n_q], count [n_q(, n_heads)] and "
+                         "idx [n_q(, n_heads), cap] expected")
     if tile > 0:
         if tiles is None:
             tiles = torch.empty((max(cap_tiles, 0), 2), dtype=torch.int32, device=dev)
@@ -108,7 +121,7 @@ def _keepset_build(m, pos, prompt_len, cap, n_keys, max_runs, count, idx, n_runs
             raise ValueError("keepset_build: tiles int32 [cap_tiles, 2], n_tiles int64 [1] expected")
     else:
         tiles = n_tiles = None
-    check(load().da_keepset_build(m, n_q, _ptr(pos), _ptr(prompt_len), n_keys, cap,
+    check(load().da_keepset_build(m, n_q, _ptr(pos), _ptr(prompt_len), n_keys, nh, _ptr(head_wb), cap,
                                   _ptr(count), _ptr(idx), max_runs, _ptr(n_runs), _ptr(runs),
                                   int(tile), _ptr(tiles), int(cap_tiles), _ptr(n_tiles),
                                   _stream(pos)),

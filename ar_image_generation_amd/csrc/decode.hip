@@ -74,7 +74,7 @@ struct DecodeArgs {
   int32_t* ws_cnt;        // [n_q][hkv] keep-set sizes (mask form, several chunks)
   const int32_t* mcount;  // the sizes the merge reads: count [n_q] (lists) or ws_cnt
   int mcount_per_head;    // mcount indexed by (query, kv head) instead of query
-  const int32_t* head_wb; // mask form: per-kv-head (W, B) [hkv][2], or null
+  const int32_t* head_wb; // mask form: per-query-head (W, B) [hq][2], or null
 };
 
 // Workspace layout: partial outputs, then partial (max, sum) pairs, then
@@ -399,7 +399,8 @@ __global__ void __launch_bounds__(256) decode_kernel(const int32_t* m0_p, const 
     const int i = i_m;
     const int P = P_m;
     const int sq_raw = sq_m;
-    // the mask's window and band, or this kv head's own (negative read as 0)
+    // the mask's window and band, or this head's own (negative read as 0;
+    // per-head masks reach this kernel with one query head per kv head)
     int Wm = a.W, Bm = a.B;
     if constexpr (PERHEAD) {
       Wm = a.head_wb[2 * g] > 0 ? a.head_wb[2 * g] : 0;

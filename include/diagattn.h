@@ -87,20 +87,24 @@ int64_t da_keep_count(const da_mask* m, int32_t pos, int32_t prompt_len, int32_t
  * and prompt_len <= max_prompt (n_keys as above); use it to size `cap`. */
 int64_t da_keep_cap(const da_mask* m, int32_t max_pos, int32_t max_prompt, int32_t n_keys);
 
-/* keepset_build -- per-query KV index lists, their maximal runs and the
- * split-KV tile list.
+/* keepset_build -- KV index lists per query (or per query and head), their
+ * maximal runs and the split-KV tile list.
  *
  * For each query q < n_q at position pos[q] with prompt_len[q] tokens of
- * prompt, writes its keep-set (rule above) as ascending positions:
- *   count[q]              number of kept keys (the true size, even if > cap;
+ * prompt and each head h < n_heads, list l = q*n_heads + h is the keep-set
+ * (rule above) of that query under head h's window and band -- head_wb[2h]
+ * and head_wb[2h+1] (device, int32; negative values read as 0), or m->W
+ * and m->B for every head when head_wb is NULL -- written as ascending
+ * positions:
+ *   count[l]              number of kept keys (the true size, even if > cap;
  *                         saturated at INT32_MAX)
- *   idx[q*cap + r]        r-th kept position, for r < min(count[q], cap)
- *   n_runs[q]             number of maximal runs of consecutive positions
- *   runs[(q*max_runs + k)*2 + {0,1}] = (first position, length) of run k,
- *                         for k < min(n_runs[q], max_runs)
- *   tiles[e*2 + {0,1}]    = (query, first entry) of tile e: each query's
- *                         first min(count[q], cap) entries cut into
- *                         consecutive chunks of `tile` entries, queries in
+ *   idx[l*cap + r]        r-th kept position, for r < min(count[l], cap)
+ *   n_runs[l]             number of maximal runs of consecutive positions
+ *   runs[(l*max_runs + k)*2 + {0,1}] = (first position, length) of run k,
+ *                         for k < min(n_runs[l], max_runs)
+ *   tiles[e*2 + {0,1}]    = (list, first entry) of tile e: each list's
+ *                         first min(count[l], cap) entries cut into
+ *                         consecutive chunks of `tile` entries, lists in
  *                         order (the work list of a split-KV decode with
  *                         split = tile), for e < min(*n_tiles, cap_tiles)
  *   *n_tiles              total number of tiles (int64, the true total)
@@ -108,19 +112,25 @@ int64_t da_keep_cap(const da_mask* m, int32_t max_pos, int32_t max_prompt, int32
  * tiles/n_tiles (then tile and cap_tiles are ignored).  Entries of idx,
  * runs and tiles past count / n_runs / n_tiles are left untouched.  The
  * summary page's custom kernels work on tiles of the kept entries (section
- * "技术方法详解", item 4); the tile list is that decomposition.
+ * "技术方法详解", item 4); the tile list is that decomposition.  Per-head
+ * windows and bands follow the summary page's future-directions section
+ * ("未来研究方向": adapting B and W) and the per-head budgets of the HeadKV
+ * abstract (thelatestinai.com page); n_heads = 1 with head_wb = NULL is the
+ * one list per query that da_sparse_decode_attn reads.
  *
  * Preconditions on device data: 0 <= pos[q]; 0 <= prompt_len[q]; for
  * causal = 0 also pos[q] < n_keys.  Queries that break them get count 0.
  * Overflow is reported, never written: if count[q] > cap (or n_runs[q] >
  * max_runs, or *n_tiles > cap_tiles) the caller's list is truncated and
  * must be treated as an error (da_keep_cap gives a safe cap).
- * Errors: DA_EINVAL for null required pointers, n_q < 0, cap < 1, W/B < 0,
- * G < 1, mode or causal out of range, causal = 0 with n_keys < 1,
- * runs/n_runs given with max_runs < 1 or only one of them given,
- * tiles/n_tiles given with tile < 1 or cap_tiles < 0 or only one given. */
+ * Errors: DA_EINVAL for null required pointers, n_q < 0, n_heads < 1,
+ * n_q * n_heads > INT32_MAX, cap < 1, W/B < 0, G < 1, mode or causal out of
+ * range, causal = 0 with n_keys < 1, runs/n_runs given with max_runs < 1 or
+ * only one of them given, tiles/n_tiles given with tile < 1 or
+ * cap_tiles < 0 or only one given, head_wb misaligned. */
 int da_keepset_build(const da_mask* m /* [host] */, int32_t n_q,
                      const int32_t* pos, const int32_t* prompt_len, int32_t n_keys,
+                     int32_t n_heads, const int32_t* head_wb,
                      int32_t cap, int32_t* count, int32_t* idx,
                      int32_t max_runs, int32_t* n_runs, int32_t* runs,
                      int32_t tile, int32_t* tiles, int64_t cap_tiles, int64_t* n_tiles,

@@ -70,25 +70,34 @@ def test_argument_errors_are_reported_before_launch():
     lib = da.load()
     m = da.mask(O.ROWDIAG, 4, 1, 3)
     dummy = ctypes.c_void_p(16)   # never dereferenced: checks fail first
-    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 0, dummy, dummy, 0, None, None, 0, None, 0, None, None)
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 1, None, 0, dummy, dummy, 0, None, None, 0, None, 0, None, None)
     assert rc == -1 and "cap" in _native.last_error()
-    rc = lib.da_keepset_build(m, -1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None)
+    rc = lib.da_keepset_build(m, -1, dummy, dummy, 0, 1, None, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None)
     assert rc == -1
-    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 2, None, dummy, 0, None, 0, None, None)
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 1, None, 4, dummy, dummy, 2, None, dummy, 0, None, 0, None, None)
     assert rc == -1 and "both" in _native.last_error()
     bad = da.mask(O.BAND, -1, 1, 3)
-    assert lib.da_keepset_build(bad, 1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None) == -1
+    assert lib.da_keepset_build(bad, 1, dummy, dummy, 0, 1, None, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None) == -1
     nc = da.mask(O.BAND, 1, 1, 3, causal=False)
-    assert lib.da_keepset_build(nc, 1, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None) == -1
+    assert lib.da_keepset_build(nc, 1, dummy, dummy, 0, 1, None, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None) == -1
     # zero queries is a valid no-op
-    assert lib.da_keepset_build(m, 0, None, None, 0, 4, None, None, 0, None, None, 0, None, 0, None, None) == 0
+    assert lib.da_keepset_build(m, 0, None, None, 0, 1, None, 4, None, None, 0, None, None, 0, None, 0, None, None) == 0
     # tile list: both pointers or neither, tile >= 1, cap_tiles >= 0
-    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 8, dummy, 4, None, None)
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 1, None, 4, dummy, dummy, 0, None, None, 8, dummy, 4, None, None)
     assert rc == -1 and "both" in _native.last_error()
-    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 0, dummy, 4, dummy, None)
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 1, None, 4, dummy, dummy, 0, None, None, 0, dummy, 4, dummy, None)
     assert rc == -1 and "tile" in _native.last_error()
-    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 4, dummy, dummy, 0, None, None, 8, dummy, -1, dummy, None)
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 1, None, 4, dummy, dummy, 0, None, None, 8, dummy, -1, dummy, None)
     assert rc == -1 and "cap_tiles" in _native.last_error()
+    # per-head lists: n_heads >= 1, n_q * n_heads within int32, head_wb aligned
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 0, dummy, 4, dummy, dummy, 0, None, None, 0, None, 0, None, None)
+    assert rc == -1 and "n_heads" in _native.last_error()
+    rc = lib.da_keepset_build(m, 1 << 20, dummy, dummy, 0, 1 << 12, dummy, 4, dummy, dummy, 0, None, None, 0, None, 0,
+                              None, None)
+    assert rc == -1 and "INT32_MAX" in _native.last_error()
+    rc = lib.da_keepset_build(m, 4, dummy, dummy, 0, 2, ctypes.c_void_p(18), 4, dummy, dummy, 0, None, None, 0, None, 0,
+                              None, None)
+    assert rc == -1 and "head_wb" in _native.last_error()
 
     kv = _native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None, 1, 1, 8)
 

@@ -216,3 +216,60 @@ def test_causal_counts_at_the_top_of_the_int32_range():
         assert count.tolist() == [ref] * 4, (mode, W, B, G)
     count, _, _, _ = build(O.DENSE, 0, 0, 1, top, np.zeros(4, dtype=np.int64), 8, max_runs=0)
     assert count.tolist() == [big, big, big - 62, big - 63]
+
+
+def test_per_head_lists_bit_exact():
+    """One list per (query, head), each under its head's window and band
+    (negative entries read as 0): lists, counts, runs and the tile list over
+    the (query, head) lists, against the oracle run per head."""
+    rng = np.random.default_rng(23)
+    for mode, G in [(O.ROWDIAG, 16), (O.ROWDIAG, 48), (O.BAND, 1), (O.DENSE, 1)]:
+        nh = 5
+        wb = np.stack([rng.integers(-3, 200, nh), rng.integers(-2, 9, nh)], axis=1).astype(np.int32)
+        wb[0] = (0, 0)
+        n_q = 70
+        prompt = rng.integers(0, 60, n_q)
+        pos = prompt + rng.integers(-5, 400, n_q)
+        pos = np.maximum(pos, 0)
+        m = da.mask(mode, 64, 2, G)
+        eff = [(max(int(w), 0), max(int(b), 0)) for w, b in wb]
+        cap = max(len(O.keepset(int(i), P=int(P), W=w, B=b, G=G, mode=mode))
+                  for i, P in zip(pos, prompt) for w, b in eff)
+        pos_t = torch.as_tensor(pos, dtype=torch.int32).to(DEV)
+        pr_t = torch.as_tensor(prompt, dtype=torch.int32).to(DEV)
+        wb_t = torch.as_tensor(wb).to(DEV)
+        count, idx, n_runs, runs = da.keepset_build(m, pos_t, pr_t, cap, max_runs=64, head_wb=wb_t)
+        _, _, tiles, n_tiles = da.keepset_tiles(m, pos_t, pr_t, cap, 7, 1 << 16, head_wb=wb_t)
+        torch.cuda.synchronize()
+        count, idx, n_runs, runs = (t.cpu().numpy() for t in (count, idx, n_runs, runs))
+        assert count.shape == (n_q, nh) and idx.shape == (n_q, nh, cap)
+        counts = []
+        for q in range(n_q):
+            for h, (w, b) in enumerate(eff):
+                ks = O.keepset(int(pos[q]), P=int(prompt[q]), W=w, B=b, G=G, mode=mode)
+                assert count[q, h] == len(ks), (mode, q, h)
+                assert np.array_equal(idx[q, h, :len(ks)], ks), (mode, q, h)
+                want_runs = O.runs(ks)
+                assert n_runs[q, h] == len(want_runs)
+                assert np.array_equal(runs[q, h, :len(want_runs)], want_runs)
+                counts.append(len(ks))
+        want = O.tiles(counts, 7)
+        assert int(n_tiles.item()) == len(want)
+        assert np.array_equal(tiles.cpu().numpy()[:len(want)], want)
+
+
+def test_per_head_lists_with_the_mask_parameters_equal_the_shared_list():
+    cfg = wl.CONFIGS["paged_b128"]
+    pos, prompt, _ = wl.positions(cfg)
+    m = da.mask(O.ROWDIAG, cfg.W, cfg.B, cfg.G)
+    cap = da.keep_cap(m, int(pos.max()), int(prompt.max()))
+    pos_t, pr_t = pos.to(DEV), prompt.to(DEV)
+    wb = torch.tensor([[cfg.W, cfg.B]] * 3, dtype=torch.int32, device=DEV)
+    c1, i1, _, _ = da.keepset_build(m, pos_t, pr_t, cap)
+    c3, i3, _, _ = da.keepset_build(m, pos_t, pr_t, cap, head_wb=wb)
+    torch.cuda.synchronize()
+    for h in range(3):
+        assert torch.equal(c3[:, h], c1)
+        for q in range(pos.numel()):
+            n = int(c1[q])
+            assert torch.equal(i3[q, h, :n], i1[q, :n])
