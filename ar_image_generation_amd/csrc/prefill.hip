@@ -499,379 +499,6 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
 }
 
 
-// ---------------------------------------------------------------- slab form
-// Row-diagonal prefill as band-shaped work.  For a 16-row block at rows
-// r0..r0+15 the kept window keys of diagonal k (|i - j - kG| <= B) lie in
-// the 32 keys starting at r0 - kG - SLAB_OFF when B <= SLAB_OFF.  So the
-// window part is one 16x32 product per (row block, diagonal) -- a "slab" --
-// instead of whole 64-key tiles whose kept density is a few percent, and
-// its mask is one 32-bit word per row and slab.  The prompt part (keys
-// j < P, kept by every row i >= P) streams in 64-key tiles.
-//
-// A workgroup's 8 row blocks are spaced G apart -- block m at rows
-// base + mG .. +15 -- so block m's diagonal k and block m+1's diagonal k+1
-// read the same slab: the workgroup streams one slab per u = m - k, used by
-// every block m with 0 <= m - u <= K (wave w holds blocks 2w and 2w+1).
-// A stage is 64 keys of K and V: a prompt tile, or the slabs u and u+1
-// (keys js..js+31 and js+G..js+G+31); stages land in a two-slot LDS ring by
-// direct copies, the next one in flight while one is computed, as in the
-// tile form above.
-constexpr int SLAB_OFF = 8;         // slab of block r0, diagonal k: keys r0 - kG - 8 ..
-constexpr int SLAB_KEYS = 32;
-constexpr int SLAB_WAVES = 4;       // waves per workgroup, two row blocks each
-constexpr int SLAB_RB = 2 * SLAB_WAVES;   // row blocks per workgroup
-constexpr int SLAB_THREADS = 64 * SLAB_WAVES;
-
-// Bits lo..hi of a 32-bit word, clipped to 0..31; 0 when the range is empty.
-__device__ inline uint32_t bits32(int lo, int hi) {
-  lo = lo < 0 ? 0 : lo;
-  hi = hi > 31 ? 31 : hi;
-  return hi < lo ? 0u : (~0u >> (31 - (hi - lo))) << lo;
-}
-
-// Keep word of one slab: keys js..js+31 for row r0 + t of a block whose
-// diagonal k the slab holds (bit c: key js + c, distance d = t + 8 + kG - c).
-// Zero unless 0 <= k <= K.  Prompt keys (j < P) are the prompt tiles'.
-__device__ inline uint32_t slab_word(int t, int k, int K, int G, int B, int W, int P, int js) {
-  if (k < 0 || k > K) return 0u;
-  const int tt = t + SLAB_OFF;
-  const int kg = k * G;
-  int lo = tt - B, hi = tt + B;                  // |d - kG| <= B
-  lo = lo > tt + kg - W ? lo : tt + kg - W;      // d <= W
-  hi = hi < tt + kg ? hi : tt + kg;              // d >= 0 (causal)
-  lo = lo > P - js ? lo : P - js;                // j >= P
-  return bits32(lo, hi);
-}
-
-template <int HD>
-__global__ void __launch_bounds__(SLAB_THREADS) __attribute__((amdgpu_waves_per_eu(2)))
-prefill_slab_kernel(PrefillArgs a) {
-  constexpr int RB = 2;                 // row blocks per wave
-  constexpr int NC = HD / 32;
-  constexpr int NB = HD / 16;
-  constexpr int CPR = HD / 8;
-  constexpr int RPI = 64 / CPR;
-  constexpr int SK = 2 * SLAB_KEYS;     // keys of a stage
-  constexpr int STILE = SK * HD;        // elements of one stage's K (or V)
-  constexpr int DPW = SK * CPR / SLAB_THREADS;
-  static_assert(DPW >= 1 && RPI * DPW * SLAB_WAVES == SK, "copies cover the stage");
-  constexpr int NS = 2;
-
-  __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * 2 * STILE];
-
-  const int t = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int lane = t & 63;
-  const int lr = lane & 15;
-  const int lg = lane >> 4;
-
-  const int n = a.n, G = a.G, Bw = a.B, W = a.W;
-  const int cpg = G / 16;               // 16-row columns per raster row
-  const int n_bh = a.batch * a.heads;
-  const int n_grp = (n + SLAB_RB * G - 1) / (SLAB_RB * G);
-  // all workgroups of (b, h) on one XCD; the last row groups (full prompt
-  // and window work) start first
-  const int bh = blockIdx.x % n_bh;
-  const int rest = blockIdx.x / n_bh;
-  const int cc = rest % cpg;
-  const int grp = n_grp - 1 - rest / cpg;
-  const int b = bh / a.heads;
-  const int h = bh % a.heads;
-  const int hk = h / (a.heads / a.kv_heads);
-  const int P = clampi(a.prompt_len[b], 0, n);
-  const int base = grp * SLAB_RB * G + 16 * cc;   // first row of block 0
-  const int K = (W + Bw) / G;                     // last diagonal reaching the window
-
-  // blocks 0..m_hi have a row below n (rows past n are computed on clamped
-  // queries and not stored)
-  const int m_hi = base < n ? ((n - 1 - base) / G < SLAB_RB - 1 ? (n - 1 - base) / G : SLAB_RB - 1) : -1;
-  const int i_max = base + m_hi * G + 15 < n - 1 ? base + m_hi * G + 15 : n - 1;
-
-  // stages: prompt tiles (keys 64s..64s+63) up to the prompt end or the
-  // last row, then slab pairs u, u+1 for u = u_lo, u_lo + 2, .. <= u_hi
-  // (slabs wholly below the prompt end hold no window key)
-  const int p_end = P < i_max + 1 ? P : i_max + 1;
-  const int S_p = m_hi < 0 ? 0 : (p_end + SK - 1) / SK;
-  int u_lo = -K;
-  {
-    const int need = P - (SLAB_KEYS - 1) - (base - SLAB_OFF);     // slab start >= need
-    const int uq = need <= 0 ? -((-need) / G) : (need + G - 1) / G;
-    u_lo = uq > u_lo ? uq : u_lo;
-  }
-  const int u_hi = m_hi;
-  const int n_slabs = u_hi >= u_lo ? u_hi - u_lo + 1 : 0;
-  const int NST = S_p + (n_slabs + 1) / 2;
-
-  const uint16_t* qb = a.q + b * a.sq[0] + h * a.sq[1];
-  const uint16_t* kb = a.k + b * a.sk[0] + hk * a.sk[1];
-  const uint16_t* vb = a.v + b * a.sv[0] + hk * a.sv[1];
-
-  auto stage_js = [&](int idx) -> int {
-    return idx < S_p ? idx * SK : base - SLAB_OFF + (u_lo + 2 * (idx - S_p)) * G;
-  };
-
-  // this lane's row and chunk in each of its copies; row r of a stage holds
-  // key js + r (prompt tile) or js + r + (r >= 32 ? G - 32 : 0) (slab pair);
-  // byte offsets from the stage's first key for both
-  int dma_row[DPW], dma_c8[DPW];
-  uint32_t dkp[DPW], dvp[DPW], dkw[DPW], dvw[DPW];
-#pragma unroll
-  for (int u = 0; u < DPW; ++u) {
-    const int blk = wave * DPW + u;
-    const int row = blk * RPI + lane / CPR;
-    const int chunk = (lane % CPR) ^ swz<CPR>(row);
-    const int64_t rw = row + (row >= SLAB_KEYS ? G - SLAB_KEYS : 0);
-    dma_row[u] = row;
-    dma_c8[u] = chunk * 8;
-    dkp[u] = (uint32_t)(((int64_t)row * a.sk[2] + chunk * 8) * 2);
-    dvp[u] = (uint32_t)(((int64_t)row * a.sv[2] + chunk * 8) * 2);
-    dkw[u] = (uint32_t)((rw * a.sk[2] + chunk * 8) * 2);
-    dvw[u] = (uint32_t)((rw * a.sv[2] + chunk * 8) * 2);
-  }
-  // stage idx into ring slot st; keys of a stage outside 0..n-1 (slabs
-  // reach before key 0 and past the last key) read a clamped row, which
-  // every mask drops
-  auto issue = [&](int idx, int st) {
-    const int js = __builtin_amdgcn_readfirstlane(stage_js(idx));
-    const bool win = idx >= S_p;
-    const int span = win ? G + SLAB_KEYS : SK;
-    uint16_t* kd = ring + st * 2 * STILE;
-    uint16_t* vd = kd + STILE;
-    if (js >= 0 && js + span <= n) {
-      const uint16_t* ks = kb + (int64_t)js * a.sk[2];
-      const uint16_t* vs = vb + (int64_t)js * a.sv[2];
-#pragma unroll
-      for (int u = 0; u < DPW; ++u) {
-        const int blk = wave * DPW + u;
-        dma16(ks, win ? dkw[u] : dkp[u], kd + blk * 512);
-        dma16(vs, win ? dvw[u] : dvp[u], vd + blk * 512);
-      }
-    } else {
-      const int j0 = clampi(js, 0, n - 1);
-      const uint16_t* ks = kb + (int64_t)j0 * a.sk[2];
-      const uint16_t* vs = vb + (int64_t)j0 * a.sv[2];
-#pragma unroll
-      for (int u = 0; u < DPW; ++u) {
-        const int blk = wave * DPW + u;
-        const int key = js + dma_row[u] + (win && dma_row[u] >= SLAB_KEYS ? G - SLAB_KEYS : 0);
-        const int r = clampi(key, 0, n - 1) - j0;                   // 0 .. span - 1
-        dma16(ks, (uint32_t)(((int64_t)r * a.sk[2] + dma_c8[u]) * 2), kd + blk * 512);
-        dma16(vs, (uint32_t)(((int64_t)r * a.sv[2] + dma_c8[u]) * 2), vd + blk * 512);
-      }
-    }
-  };
-
-  if (NST > 0) issue(0, 0);
-
-  // wave w: blocks m = 2w + rb; lane lr of block rb holds row r0[rb] + lr
-  int r0[RB];
-  bf16x8 qv[RB][NC];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    r0[rb] = base + (2 * wave + rb) * G;
-    const int i = r0[rb] + lr;
-    const uint16_t* qrow = qb + (int64_t)(i < n ? i : n - 1) * a.sq[2];
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qv[rb][c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + lg * 8);
-  }
-
-  float mq[RB], ls[RB];
-  f32x4 o[RB][NB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    mq[rb] = -INFINITY;
-    ls[rb] = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o[rb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int vt_row = 4 * lg + (lr >> 2);
-  const int vt_sub = lr & 3;
-
-  // One stage: the participating row blocks (SEL bit rb) take S^T = K Q^T
-  // over the stage's 64 keys, apply their keep words (unless wholly kept),
-  // update the running max and sum, and add V^T P^T.
-  auto compute = [&](const uint16_t* st0, auto sel, const uint64_t (&word)[RB], const bool (&full)[RB]) {
-    constexpr int SEL = decltype(sel)::value;
-    f32x4 sc[RB][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq) sc[rb][kq] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // two 16-key blocks at a time: their K operand reads first, then the
-    // products with the (row block, key block) chains interleaved
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      bf16x8 kf[2][NC];
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int row = 16 * (2 * kp + q2) + lr;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-          kf[q2][c] = *reinterpret_cast<const bf16x8*>(st0 + row * HD + (((4 * c + lg) ^ swz<CPR>(row)) * 8));
-      }
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            if (SEL & (1 << rb))
-              sc[rb][2 * kp + q2] =
-                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[q2][c], qv[rb][c], sc[rb][2 * kp + q2], 0, 0, 0);
-    }
-    // key 16kq + 4lg + r of the stage: bit 16kq + r of word >> 4lg
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (!(SEL & (1 << rb)) || full[rb]) continue;
-      const uint64_t sh = word[rb] >> (4 * lg);
-      const uint32_t wd[2] = {(uint32_t)sh, (uint32_t)(sh >> 32)};
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int32_t mk = (int32_t)(wd[kq >> 1] << (31 - (16 * (kq & 1) + r))) >> 31;
-          sc[rb][kq][r] = __int_as_float((__float_as_int(sc[rb][kq][r]) & mk) | (~mk & (int32_t)0xff800000));
-        }
-    }
-    float mts[RB];
-    bool grow = false;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (!(SEL & (1 << rb))) continue;
-      float mt = -INFINITY;
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[rb][kq][r]);
-      mts[rb] = max_over_row_groups(mt) * a.qscale;
-      grow = grow || mts[rb] > mq[rb] + 8.f;
-    }
-    if (__any(grow)) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if (!(SEL & (1 << rb))) continue;
-        const float mn = fmaxf(mq[rb], mts[rb]);
-        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mq[rb] - mn);
-        ls[rb] *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[rb][nb][r] *= alpha;
-        mq[rb] = mn;
-      }
-    }
-    bf16x8 pb[RB][2];                   // P^T of the stage's two 32-key chunks
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      if (!(SEL & (1 << rb))) continue;
-      const float mref = mq[rb] == -INFINITY ? 0.f : mq[rb];
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[rb][2 * ch + e / 4][e % 4], a.qscale, -mref));
-          ls[rb] += p;
-          pb[rb][ch][e] = (__bf16)p;
-        }
-    }
-    // O^T += V^T P^T, one 32-key chunk at a time: its V^T operand reads
-    // first, then the products
-    const uint16_t* vsm = st0 + STILE;
-#pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
-      bf16x8 vf[NB];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int chunk = 2 * nb + (vt_sub >> 1);
-        const int r_lo = 32 * ch + vt_row, r_hi = r_lo + 16;
-        const uint16_t* plo = vsm + r_lo * HD + ((chunk ^ swz<CPR>(r_lo)) * 8) + (vt_sub & 1) * 4;
-        const uint16_t* phi = vsm + r_hi * HD + ((chunk ^ swz<CPR>(r_hi)) * 8) + (vt_sub & 1) * 4;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
-        typedef short v8i16 __attribute__((ext_vector_type(8)));
-        const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        vf[nb] = __builtin_bit_cast(bf16x8, w);
-      }
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          if (SEL & (1 << rb))
-            o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nb], pb[rb][ch], o[rb][nb], 0, 0, 0);
-    }
-  };
-
-  // Step idx: stage idx is in flight (the only one this wave issued since
-  // the last wait).  Each wave waits for its own copies of it, the barrier
-  // covers every wave's copies and the end of step idx-1, whose slot then
-  // receives stage idx+1 while this one is computed.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the queries and stage 0
-  auto step = [&](int idx, auto slot) {
-    constexpr int ST = decltype(slot)::value;
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __builtin_amdgcn_s_barrier();
-    __asm__ volatile("" ::: "memory");
-    if (idx + 1 < NST) issue(idx + 1, (ST + 1) % NS);
-
-    const int js = stage_js(idx);
-    bool part[RB], full[RB];
-    uint64_t word[RB];
-    if (idx < S_p) {
-      // prompt keys js..js+63: row i keeps j < P and j <= i
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int m = 2 * wave + rb;
-        part[rb] = m <= m_hi && js <= r0[rb] + 15;
-        full[rb] = js + SK - 1 < P && js + SK - 1 <= r0[rb];
-        const int i = r0[rb] + lr;
-        word[rb] = bit_range(0, (P - 1 < i ? P - 1 : i) - js);
-      }
-    } else {
-      // slabs u (keys js..) and u+1 (keys js+G..): block m reads them for
-      // diagonals m - u and m - u - 1
-      const int u = u_lo + 2 * (idx - S_p);
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const int m = 2 * wave + rb;
-        const int k0 = m - u;
-        part[rb] = m <= m_hi && r0[rb] + 15 >= P && k0 >= 0 && k0 - 1 <= K;
-        full[rb] = false;
-        const uint32_t w0 = slab_word(lr, k0, K, G, Bw, W, P, js);
-        const uint32_t w1 = slab_word(lr, k0 - 1, K, G, Bw, W, P, js + G);
-        word[rb] = (uint64_t)w0 | ((uint64_t)w1 << 32);
-      }
-    }
-    const uint16_t* st0 = ring + ST * 2 * STILE;
-    if (part[0] && part[1]) compute(st0, std::integral_constant<int, 3>{}, word, full);
-    else if (part[0]) compute(st0, std::integral_constant<int, 1>{}, word, full);
-    else if (part[1]) compute(st0, std::integral_constant<int, 2>{}, word, full);
-  };
-  for (int idx = 0; idx < NST; idx += NS) {
-    step(idx, std::integral_constant<int, 0>{});
-    if (idx + 1 < NST) step(idx + 1, std::integral_constant<int, 1>{});
-  }
-
-  // ---- normalise and store: lane holds row r0[rb] + lr, dims 16nb + 4lg + r
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float L = sum_over_row_groups(ls[rb]);
-    const int i = r0[rb] + lr;
-    if (2 * wave + rb > m_hi || i >= n) continue;
-    const float inv = 1.f / L;
-    uint16_t* orow = a.o + b * a.so[0] + h * a.so[1] + (int64_t)i * a.so[2];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint32_t w0 = f32_to_bf16(o[rb][nb][0] * inv) | (f32_to_bf16(o[rb][nb][1] * inv) << 16);
-      const uint32_t w1 = f32_to_bf16(o[rb][nb][2] * inv) | (f32_to_bf16(o[rb][nb][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(orow + 16 * nb + 4 * lg) = make_uint2(w0, w1);
-    }
-    if (a.lse && lg == 0)
-      a.lse[((int64_t)b * a.heads + h) * n + i] = (mq[rb] + log2f(L)) * kLn2P;
-  }
-}
-
 }  // namespace da
 
 using namespace da;
@@ -981,20 +608,6 @@ extern "C" int da_band_prefill_attn(const da_mask* m, da_dtype dtype, int32_t ba
   a.heads = heads;
   a.kv_heads = kv_heads;
   a.qscale = scale * kLog2eP;
-  // row-diagonal masks whose bands fit a 32-key slab (B <= 8), with one
-  // diagonal per kept pair (2B + 1 < G) and raster rows of whole 16-row
-  // blocks (G a multiple of 16): the slab form
-  // (and the slab pair's span, G + 32 keys, addressable by 32-bit offsets)
-  const bool slab_span_ok = ((int64_t)(a.G + SLAB_KEYS) * a.sk[2] + head_dim) * 2 <= (int64_t)UINT32_MAX &&
-                            ((int64_t)(a.G + SLAB_KEYS) * a.sv[2] + head_dim) * 2 <= (int64_t)UINT32_MAX;
-  if (m->mode == DA_MODE_ROWDIAG && a.G % 16 == 0 && a.B <= SLAB_OFF && 2 * a.B + 1 < a.G && slab_span_ok) {
-    const int64_t n_grp = ((int64_t)n + SLAB_RB * (int64_t)a.G - 1) / (SLAB_RB * (int64_t)a.G);
-    const int64_t sblocks = (int64_t)batch * heads * n_grp * (a.G / 16);
-    if (sblocks > 0x7fffffff) return fail(DA_ENOTSUP, "grid too large");
-    void (*sfn)(PrefillArgs) = head_dim == 128 ? prefill_slab_kernel<128> : prefill_slab_kernel<64>;
-    hipLaunchKernelGGL(sfn, dim3((unsigned)sblocks), dim3(SLAB_THREADS), 0, (hipStream_t)stream, a);
-    return check_launch("prefill_slab_kernel");
-  }
   const int64_t blocks = (int64_t)a.n_qt * batch * heads;
   if (blocks > 0x7fffffff) return fail(DA_ENOTSUP, "grid too large");
   void (*fn)(PrefillArgs);

@@ -369,11 +369,7 @@ int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t
  * whole sequence is attended at once.  Only the key tiles listed in `tiles`
  * (da_prefill_tiles_build with the same mask, n and prompt_len) are
  * computed; element masks (a 64-bit keep word per row and key tile) are
- * applied where a wave's blocks are not all entirely kept.  Row-diagonal
- * masks with B <= 8, 2B + 1 < G and G a multiple of 16 take a band-shaped
- * form instead: the prompt keys in 64-key tiles and, per 16-row block and
- * raster-row diagonal k, only the 32 keys around i - kG; that form does not
- * read `tiles` (it must still be given, of the size below).
+ * applied where a wave's blocks are not all entirely kept.
  *
  *   q, out [batch][heads][n][head_dim], k, v [batch][kv_heads][n][head_dim],
  *          bf16, head_dim elements contiguous and 16-byte aligned;

@@ -151,11 +151,11 @@ def test_random_masks_and_shapes(seed):
                                           (1, 0, 4, 1, 16, 128), (1100, 256, 256, 3, 64, 128),
                                           (260, 260, 64, 3, 32, 64), (700, 31, 2**31 - 1, 8, 64, 128),
                                           (1030, 0, 160, 5, 80, 128)])
-def test_row_diagonal_slab_shapes(n, P, W, B, G, hd):
-    """Row-diagonal masks whose bands fit 32-key slabs (B <= 8, 2B + 1 < G,
-    G a multiple of 16): ragged lengths, prompts longer than the sequence,
-    windows past the sequence, the widest band, a group of query heads per
-    kv head.  Every row against the oracle."""
+def test_row_diagonal_shapes(n, P, W, B, G, hd):
+    """Row-diagonal masks at raster widths of 16 to 80 with bands up to 8:
+    ragged lengths, prompts longer than the sequence, windows past the
+    sequence, a group of query heads per kv head.  Every row against the
+    oracle."""
     q = randn((2, 4, n, hd), 31)
     k, v = randn((2, 2, n, hd), 32), randn((2, 2, n, hd), 33)
     prompt = [P, n // 3]
