@@ -8,6 +8,7 @@ from .api import (  # noqa: F401
     DENSE,
     ROWDIAG,
     band_prefill_attn,
+    decode_schedule,
     decode_workspace,
     decode_workspace_bytes,
     hbm_read_probe,

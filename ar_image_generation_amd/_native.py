@@ -49,6 +49,7 @@ SIGNATURES = {
     "da_ring_block_table": (ctypes.c_int, [ctypes.POINTER(DaMask), c_i32, c_vp, c_i32, c_i32, c_i32,
                                            c_i32, c_vp, c_vp]),
     "da_decode_scratch_bytes": (c_i64, []),
+    "da_decode_schedule": (ctypes.c_int, [c_vp, c_i32, c_i32, c_i32, c_vp]),
     "da_sparse_decode_attn_masked_noalloc": (ctypes.c_int, [ctypes.POINTER(DaMask), c_vp, ctypes.c_int,
                                                             c_i32, c_i32, c_i32, c_i32, c_f32,
                                                             ctypes.POINTER(DaKvCache), c_vp, c_vp,

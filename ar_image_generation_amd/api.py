@@ -340,6 +340,19 @@ def ring_block_table(m: DaMask, prompt_len, max_len: int, page_size: int, first_
     return bt, int(total.value)
 
 
+def decode_schedule(cost, wg_per_query: int, n_cu: int = 0) -> torch.Tensor:
+    """Batch order balancing the decode step over the compute units: cost
+    = host per-query work (e.g. keep_count of each query), wg_per_query =
+    workgroups a query launches (hkv).  Returns an int32 CPU tensor: the
+    query for each batch slot."""
+    c = torch.as_tensor(cost, dtype=torch.int64).contiguous()
+    order = torch.empty(c.numel(), dtype=torch.int32)
+    check(load().da_decode_schedule(c.data_ptr(), c.numel(), int(wg_per_query), int(n_cu),
+                                    order.data_ptr()),
+          "da_decode_schedule")
+    return order
+
+
 def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int,
                    nbytes: Optional[int] = None, offset: int = 0, loads_in_flight: int = 8) -> None:
     """Streams `nbytes` bytes of `buf` starting at byte `offset` (measurement)."""

@@ -20,7 +20,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdiagattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "keepset.hip", "decode.hip", "probe.hip", "prefill.hip", "residency.hip"]
+SOURCES = ["api.hip", "keepset.hip", "decode.hip", "probe.hip", "prefill.hip", "residency.hip",
+           "schedule.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

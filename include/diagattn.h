@@ -401,6 +401,28 @@ int da_band_prefill_attn(const da_mask* m /* [host] */, da_dtype dtype, int32_t 
                          const void* tiles, int64_t tiles_bytes, float scale, float* lse,
                          void* stream);
 
+/* [host] decode_schedule -- a batch order that balances the decode step's
+ * kept rows over the compute units.
+ *
+ * cost[q] (host, >= 0) is query q's work, e.g. da_keep_count of its position
+ * and prompt length; wg_per_query is the number of workgroups the decode
+ * launches per query (hkv for one chunk a list); n_cu the compute units (0:
+ * those of the current device).  Writes order[p] (host), a permutation of
+ * 0..n-1: the query to place in batch slot p.  Workgroups are dealt to the
+ * compute units in turn, so the slots p, p + R, p + 2R, ... (R = n_cu /
+ * wg_per_query, at least 1) share compute units; queries are taken largest
+ * first, R a round, each into the round's slot group with the least cost so
+ * far.  The decode step of a batch laid out in this order computes the same
+ * outputs for every query (only their slots move) and ends sooner when
+ * costs differ: the last compute unit to finish has less work.  This is a
+ * scheduling aid for the serving layer around the step, which knows each
+ * request's prompt length and position (the summary page's serving system,
+ * "技术方法详解" item 4, schedules requests around its sparse kernels).
+ * Errors: DA_EINVAL (n < 0, wg_per_query < 1, n_cu < 0, a negative cost,
+ * null pointers), DA_EHIP (n_cu = 0 and no device). */
+int da_decode_schedule(const int64_t* cost /* [host] */, int32_t n, int32_t wg_per_query, int32_t n_cu,
+                       int32_t* order /* [host] */);
+
 /* Measurement: streaming read of `bytes` bytes at `buf` (16-byte aligned, a
  * multiple of 16) by `grid` workgroups of 256 threads, 16-byte nontemporal
  * loads, `loads_in_flight` (1, 2, 4, 8 or 16) independent loads per thread

@@ -432,3 +432,31 @@ def test_long_context(dtype):
                                           pos.numpy(), prompt.numpy(), seq.numpy(),
                                           W=256, B=3, G=64, mode=mode)
         assert_close(o2.cpu(), l2.cpu(), ref_o, ref_l, dtype)
+
+
+def test_scheduled_batch_order_moves_only_slots():
+    """The batch laid out in da_decode_schedule's order (the serving-layer
+    layout the benchmark times) gives every query bit for bit the output,
+    LSE and keep-set list it gets in the generated order."""
+    cfg = wl.CONFIGS["paged_b128"]
+    inp = wl.decode_inputs(cfg)
+    m = da.mask(cfg.modes[0], cfg.W, cfg.B, cfg.G)
+    cost = [da.keep_count(m, int(p), int(P)) for p, P in zip(inp.pos.tolist(), inp.prompt_len.tolist())]
+    perm = da.decode_schedule(cost, cfg.hkv).long()
+    assert sorted(perm.tolist()) == list(range(inp.n_q))
+    cap = max(cost)
+    k, v, bt = caches(inp)
+    res = []
+    for p in (torch.arange(inp.n_q), perm):
+        q = inp.q[p].contiguous().to(dev())
+        o, lse, c, i = da.sparse_decode_attn_masked(
+            m, q, k, v, inp.seq[p].contiguous().to(dev()), inp.pos[p].contiguous().to(dev()),
+            inp.prompt_len[p].contiguous().to(dev()), cap=cap, split=4096, block_table=bt,
+            want_lse=True, want_lists=True)
+        torch.cuda.synchronize()
+        res.append((o.cpu(), lse.cpu(), c.cpu(), i.cpu()))
+    (o0, l0, c0, i0), (o1, l1, c1, i1) = res
+    assert torch.equal(o1, o0[perm]) and torch.equal(l1, l0[perm]) and torch.equal(c1, c0[perm])
+    for slot in range(inp.n_q):
+        n = int(c1[slot])
+        assert torch.equal(i1[slot, :n], i0[perm[slot], :n])
