@@ -746,7 +746,8 @@ def summarize(args):
     avg = sum(durs) / len(durs) if durs else float("nan")
     lines = [
         f"# rocprofv3 summary: decode kernel of the benchmark step (keep-set computed in the "
-        f"kernel, lists written, attention), workload {cfg.name}",
+        f"kernel, lists written, attention), workload {cfg.name}, batch in the slots "
+        f"da_decode_schedule gives its queries",
         "# commands (repo root, TMPDIR=/tmp):",
         f"#   rocprofv3 --kernel-trace --stats -f csv -d {trace_dir} -o run -- python3 bench.py --profile-run --workload {cfg.name} --steps {args.steps} --warmup {args.warmup}",
         f"#   rocprofv3 --pmc FETCH_SIZE -f csv -d {fetch_dir} -o run -- python3 bench.py --profile-run --workload {cfg.name} --steps {args.steps} --warmup {args.warmup}",
