@@ -679,15 +679,15 @@ __global__ void __launch_bounds__(256) decode_kernel(const int32_t* m0_p, const 
 // arithmetic, not its loads, set its speed on the GQA workloads).
 //
 // Layout.  Each wave takes blocks of 16 kept rows (wave w: blocks w, w+4,
-// ...).  Lane l loads, for row l % 16 of the block, the 64 bytes of K and of
-// V at dims 32c + 8 (l / 16) .. + 8, c = 0 .. HD/32 - 1: that is the A
-// operand of S^T = K Q^T as loaded, so K goes straight from its load into
-// the matrix core.  The result gives lane l the scores of rows 4 (l/16) + r,
+// ...), loaded as whole rows (RPI rows a wave instruction, 16 bytes a lane)
+// into registers and staged in a 4 KiB LDS area of the wave: K comes back
+// as the A operand of S^T = K Q^T (lane l: row l % 16, dims 32c + 8 (l/16)
+// .. + 8), V comes back transposed (ds_read_b64_tr_b16) as the A operand
+// V^T.  The score result gives lane l the scores of rows 4 (l/16) + r,
 // r = 0..3, for query head l % 16 -- the layout of the B operand P^T of the
-// second product, so the softmax runs in place.  V goes through a 4 KiB LDS
-// staging area of the wave and comes back transposed (ds_read_b64_tr_b16)
-// as the A operand V^T.  Two blocks are in flight per wave (K and V in
-// registers); loads are nontemporal (each byte is read once).  The online
+// second product, so the softmax runs in place.  The next block's K and V
+// are in flight while a block is computed; loads are nontemporal (each
+// byte is read once).  The online
 // softmax keeps a reference max per query head that moves only when the
 // block max passes it by more than 2^8 (log2 domain), so the output
 // accumulators are rescaled rarely.  Rows (element offsets, and positions
@@ -909,7 +909,7 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
   const int nblk = (nrows + 15) / 16;
   uint16_t* vst = stage + wave * (VST > RED ? VST : RED);
 
-  // ---- stage 2: blocks of 16 rows, two in flight per wave
+  // ---- stage 2: blocks of 16 rows, the next one in flight per wave
   float m = -INFINITY, lsum = 0.f;
   f32x4 o[NB];
 #pragma unroll
