@@ -49,7 +49,7 @@ int check_mask(const da_mask* m) {
 
 using namespace da;
 
-extern "C" int32_t da_version(void) { return 200; }
+extern "C" int32_t da_version(void) { return 300; }
 
 extern "C" const char* da_last_error(void) { return g_err; }
 

@@ -27,7 +27,9 @@
  * Conventions.
  *   - Every pointer is a DEVICE pointer owned by the caller unless marked
  *     [host].  The library allocates no memory and keeps no state besides a
- *     thread-local error string.
+ *     thread-local error string and, on each GPU, the fixed scratch array
+ *     of da_sparse_decode_attn_masked_noalloc (part of the loaded code
+ *     object).
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  No call synchronises the device or copies host<->device.
  *   - Host-checkable argument errors return a negative da_status before any
