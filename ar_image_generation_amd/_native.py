@@ -44,7 +44,7 @@ SIGNATURES = {
                                             ctypes.POINTER(c_i64), c_vp, c_vp, c_i64, c_f32, c_vp, c_vp]),
     "da_sparse_decode_attn": (ctypes.c_int, [c_vp, ctypes.c_int, c_i32, c_i32, c_i32, c_i32, c_f32,
                                              ctypes.POINTER(DaKvCache), c_vp, c_vp, c_vp, c_i32,
-                                             c_i32, c_vp, c_vp, c_vp, c_i64, c_vp]),
+                                             c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_vp]),
     "da_ring_pages": (c_i64, [ctypes.POINTER(DaMask), c_i32, c_i32, c_i32]),
     "da_ring_block_table": (ctypes.c_int, [ctypes.POINTER(DaMask), c_i32, c_vp, c_i32, c_i32, c_i32,
                                            c_i32, c_vp, c_vp]),

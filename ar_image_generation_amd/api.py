@@ -177,9 +177,11 @@ def sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
                        split: int, block_table: Optional[torch.Tensor] = None,
                        scale: Optional[float] = None, out=None, lse=None,
                        want_lse: bool = False, workspace=None):
-    """q [n_q, hq, hd]; caches as in ``kv_cache``; seq/count [n_q] int32;
-    idx [n_q, cap] int32.  ``workspace``: from ``decode_workspace`` (reusable
-    across calls on one stream); allocated per call when omitted.
+    """q [n_q, hq, hd]; caches as in ``kv_cache``; seq [n_q] int32; one list
+    per query, count [n_q] and idx [n_q, cap] int32, or one per kv head,
+    count [n_q, hkv] and idx [n_q, hkv, cap] (``keepset_build`` with a
+    [hkv, 2] ``head_wb``).  ``workspace``: from ``decode_workspace``
+    (reusable across calls on one stream); allocated per call when omitted.
     Returns (out [n_q, hq, hd], lse [n_q, hq] or None)."""
     _need_cuda("sparse_decode_attn", q, k_cache, v_cache, seq, count, idx, block_table)
     if q.dim() != 3 or not q.is_contiguous():
@@ -188,12 +190,15 @@ def sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
         raise ValueError("q and the caches must share dtype fp32 or bf16")
     n_q, hq, hd = q.shape
     hkv = k_cache.shape[1]
-    if idx.dim() != 2 or idx.shape[0] != n_q or not idx.is_contiguous() or idx.dtype != torch.int32:
-        raise ValueError("idx must be a contiguous int32 [n_q, cap] tensor")
-    for t in (seq, count):
-        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != n_q:
-            raise ValueError("seq and count must be contiguous int32 [n_q] tensors")
-    cap = idx.shape[1]
+    lh = hkv if idx.dim() == 3 else 1
+    if idx.dim() not in (2, 3) or idx.shape[0] != n_q or (lh > 1 and idx.shape[1] != hkv) or \
+            not idx.is_contiguous() or idx.dtype != torch.int32:
+        raise ValueError("idx must be a contiguous int32 [n_q, cap] or [n_q, hkv, cap] tensor")
+    if seq.dtype != torch.int32 or not seq.is_contiguous() or seq.numel() != n_q:
+        raise ValueError("seq must be a contiguous int32 [n_q] tensor")
+    if count.dtype != torch.int32 or not count.is_contiguous() or count.numel() != n_q * lh:
+        raise ValueError("count must be a contiguous int32 tensor of n_q (or n_q * hkv) entries")
+    cap = idx.shape[-1]
     if scale is None:
         scale = 1.0 / math.sqrt(hd)
     if out is None:
@@ -205,7 +210,7 @@ def sparse_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     kv = kv_cache(k_cache, v_cache, block_table)
     check(load().da_sparse_decode_attn(_ptr(q), _DTYPE[q.dtype], n_q, hq, hkv, hd, float(scale),
-                                       kv, _ptr(seq), _ptr(count), _ptr(idx), cap, split,
+                                       kv, _ptr(seq), _ptr(count), _ptr(idx), cap, lh, split,
                                        _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                        _stream(q)),
           "da_sparse_decode_attn")

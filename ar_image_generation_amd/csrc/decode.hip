@@ -74,6 +74,7 @@ struct DecodeArgs {
   int32_t* ws_cnt;        // [n_q][hkv] keep-set sizes (mask form, several chunks)
   const int32_t* mcount;  // the sizes the merge reads: count [n_q] (lists) or ws_cnt
   int mcount_per_head;    // mcount indexed by (query, kv head) instead of query
+  int list_heads;         // list form: lists per query, 1 or hkv (list q*hkv + g per kv head)
   const int32_t* head_wb; // mask form: per-query-head (W, B) [hq][2], or null
 };
 
@@ -331,14 +332,16 @@ __global__ void __launch_bounds__(256) decode_kernel(const int32_t* m0_p, const 
     }
   };
   if constexpr (!MASKED) {
-    const int32_t* myidx = m1_p + (int64_t)qi * cap_p + r0;
+    // the query's list, or with one list per kv head this kv head's
+    const int lrow = a.list_heads > 1 ? qg : qi;
+    const int32_t* myidx = m1_p + (int64_t)lrow * cap_p + r0;
     int jj[IPT];
 #pragma unroll
     for (int u = 0; u < IPT; ++u) {
       const int r = u * 256 + t;
       jj[u] = myidx[r < lim ? r : lim - 1];
     }
-    cnt = m0_p[qi];
+    cnt = m0_p[lrow];
     const int sq_raw = seq_p[qi];
     // compiler-only barrier: keeps the loads above ahead of the count test
     // (they would otherwise be sunk behind it), with the argument-block
@@ -735,7 +738,8 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
     P_m = m1_p[qi];
     sq_m = seq_p[qi];
   } else {
-    cnt_l = m0_p[qi];
+    // the query's list, or with one list per kv head this kv head's
+    cnt_l = m0_p[a.list_heads > 1 ? qg : qi];
     sq_m = seq_p[qi];
   }
   const int r0 = s * split_p;
@@ -836,7 +840,7 @@ __global__ void __launch_bounds__(256) decode_mfma_kernel(const int32_t* m0_p, c
   {
     // IPT rows a thread a round; only as many rows as the chunk has are
     // computed (a closed-form entry costs an integer division)
-    const int32_t* myidx = MASKED ? nullptr : m1_p + (int64_t)qi * cap_p + r0;
+    const int32_t* myidx = MASKED ? nullptr : m1_p + (int64_t)(a.list_heads > 1 ? qg : qi) * cap_p + r0;
     auto fill = [&](auto ipt) {
       constexpr int IPT = decltype(ipt)::value;
       for (int base = 0; base < nrows; base += IPT * 256) {
@@ -1304,6 +1308,7 @@ static int prepare_decode(DecodeArgs& a, const void* q, da_dtype dtype, int32_t 
   if (blocks > 0x7fffffff) return fail(DA_ENOTSUP, "grid of %lld workgroups too large", (long long)blocks);
 
   a = DecodeArgs{};
+  a.list_heads = 1;
   a.q = q;
   a.k = kv->k;
   a.v = kv->v;
@@ -1384,19 +1389,23 @@ extern "C" int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
                                      int32_t hkv, int32_t head_dim, float scale,
                                      const da_kv_cache* kv, const int32_t* seq,
                                      const int32_t* count, const int32_t* idx, int32_t cap,
-                                     int32_t split, void* out, float* lse, void* workspace,
-                                     int64_t ws_bytes, void* stream) {
+                                     int32_t list_heads, int32_t split, void* out, float* lse,
+                                     void* workspace, int64_t ws_bytes, void* stream) {
   DecodeArgs a;
   int rc = prepare_decode(a, q, dtype, n_q, hq, hkv, head_dim, scale, kv, seq, cap, split, out, lse,
                           workspace, ws_bytes);
   if (rc) return rc;
   if (n_q > 0 && (!count || !idx)) return fail(DA_EINVAL, "count and idx must be non-NULL");
+  if (list_heads != 1 && list_heads != hkv)
+    return fail(DA_EINVAL, "list_heads=%d must be 1 or hkv=%d", list_heads, hkv);
   clear_error();
   if (n_q == 0) return DA_OK;
   a.count = count;
   a.idx = idx;
-  a.mcount = count;
-  a.ws_cnt = nullptr;                   // the merge reads the lists' counts
+  a.list_heads = list_heads;
+  a.mcount = count;                     // the merge reads the lists' counts
+  a.mcount_per_head = list_heads > 1;
+  a.ws_cnt = nullptr;
   return launch_decode<0>(a, dtype, head_dim, stream);
 }
 

@@ -194,7 +194,11 @@ int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t head_dim,
  *   out   [n_q][hq][head_dim] in `dtype`
  *   lse   [n_q][hq] fp32 natural-log sum of exp of the scaled logits, or NULL
  *   seq   [n_q] request (block-table row) of each query
- *   count [n_q], idx [n_q][cap] as written by da_keepset_build
+ *   count [n_q], idx [n_q][cap] as written by da_keepset_build; or, with
+ *         list_heads = hkv, one list per kv head: count [n_q][hkv],
+ *         idx [n_q][hkv][cap] (da_keepset_build with n_heads = hkv and a
+ *         (W, B) per kv head), kv head g of query q attending list q*hkv + g
+ *         -- per-kv-head budgets; list_heads must be 1 or hkv
  *   workspace: da_decode_workspace_bytes(...) bytes, 256-byte aligned, or
  *         NULL when that is 0; no initialisation needed.  Calls that share a
  *         workspace must not overlap in time (one workspace per stream).
@@ -203,13 +207,14 @@ int64_t da_decode_workspace_bytes(int32_t n_q, int32_t hq, int32_t head_dim,
  * clamped into the descriptor's extents (see da_kv_cache).
  * Errors: DA_EINVAL (null pointers, n_q < 0, hq or hkv < 1, hq % hkv != 0,
  * cap < 1, split < 1, non-power-of-two page_size with a block table,
- * bt_stride < 1, extents < 1, max_len > bt_stride * page_size), DA_ENOTSUP (head_dim not 64/128, dtype, hq/hkv not in
+ * bt_stride < 1, extents < 1, max_len > bt_stride * page_size, list_heads
+ * not 1 or hkv), DA_ENOTSUP (head_dim not 64/128, dtype, hq/hkv not in
  * {1,2,4,8}, split > 4096), DA_ECAPACITY (workspace too small). */
 int da_sparse_decode_attn(const void* q, da_dtype dtype, int32_t n_q,
                           int32_t hq, int32_t hkv, int32_t head_dim, float scale,
                           const da_kv_cache* kv /* [host] */, const int32_t* seq,
                           const int32_t* count, const int32_t* idx, int32_t cap,
-                          int32_t split, void* out, float* lse,
+                          int32_t list_heads, int32_t split, void* out, float* lse,
                           void* workspace, int64_t ws_bytes, void* stream);
 
 /* sparse_decode_attn_masked -- the same decode step with the keep-set taken

@@ -101,9 +101,9 @@ def test_argument_errors_are_reported_before_launch():
 
     kv = _native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None, 1, 1, 8)
 
-    def dec(dtype=1, n_q=1, hq=8, hkv=2, hd=128, cap=64, split=64, ws=None, wsb=0, kvd=kv, q=dummy):
+    def dec(dtype=1, n_q=1, hq=8, hkv=2, hd=128, cap=64, split=64, ws=None, wsb=0, kvd=kv, q=dummy, lh=1):
         return lib.da_sparse_decode_attn(q, dtype, n_q, hq, hkv, hd, 0.1, kvd, dummy, dummy,
-                                         dummy, cap, split, dummy, None, ws, wsb, None)
+                                         dummy, cap, lh, split, dummy, None, ws, wsb, None)
     assert dec(hq=6, hkv=4) == -1
     assert dec(hd=96) == -2
     assert dec(dtype=3) == -2
@@ -119,6 +119,8 @@ def test_argument_errors_are_reported_before_launch():
     assert dec(kvd=_native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None, 1, 1, 0)) == -1
     assert dec(kvd=_native.DaKvCache(16, 16, 0, 0, 0, 0, 0, None, 3, 2, 8)) == -1
     assert dec(q=ctypes.c_void_p(8)) == -1   # misaligned q
+    assert dec(lh=3) == -1 and "list_heads" in _native.last_error()   # lists: one a query or one a kv head
+    assert dec(lh=2, n_q=0) == 0
 
     def dec_m(mk=m, n_q=1, hq=8, hkv=2, hd=128, cap=64, split=64, pos=dummy, count=None, idx=None,
               k_new=None, v_new=None, head_wb=None):

@@ -460,3 +460,37 @@ def test_scheduled_batch_order_moves_only_slots():
     for slot in range(inp.n_q):
         n = int(c1[slot])
         assert torch.equal(i1[slot, :n], i0[perm[slot], :n])
+
+
+@pytest.mark.parametrize("name,split", [("gqa_b64", 4096), ("gqa_b64", 37), ("paged_b128", 4096),
+                                        ("llamagen_b16", 4096), ("llamagen_b16", 50)])
+def test_per_kv_head_lists(name, split):
+    """One list per kv head (the builder with a (W, B) per kv head) through
+    the list decode: every query head against the oracle run with its kv
+    head's mask, and bitwise the mask form with those (W, B) given per
+    query head.  Splits below the list lengths exercise the merge, which
+    then reads the counts per (query, kv head)."""
+    cfg = wl.small_decode(name, n_seq=3)
+    inp = wl.decode_inputs(cfg)
+    k, v, bt = caches(inp)
+    grp = cfg.hq // cfg.hkv
+    rng = np.random.default_rng(31)
+    wb_kv = np.stack([rng.integers(0, 300, cfg.hkv), rng.integers(0, 7, cfg.hkv)], axis=1).astype(np.int32)
+    wb_q = np.repeat(wb_kv, grp, axis=0)
+    q, seq = inp.q.to(dev()), inp.seq.to(dev())
+    pos, prompt = inp.pos.to(dev()), inp.prompt_len.to(dev())
+    maxpos, maxp = int(inp.pos.max()), int(inp.prompt_len.max())
+    for mode in (O.BAND, O.ROWDIAG):
+        m = da.mask(mode, cfg.W, cfg.B, cfg.G)
+        cap = da.keep_cap(m, maxpos, maxp, head_wb=wb_kv)
+        count, idx, _, _ = da.keepset_build(m, pos, prompt, cap, head_wb=torch.from_numpy(wb_kv).to(dev()))
+        ws = da.decode_workspace(inp.n_q, cfg.hq, cfg.hd, cap, split, dev())
+        out, lse = da.sparse_decode_attn(q, k, v, seq, count, idx, split=split, block_table=bt,
+                                         want_lse=True, workspace=ws)
+        o2, l2, _, _ = da.sparse_decode_attn_masked(m, q, k, v, seq, pos, prompt, cap=cap, split=split,
+                                                    block_table=bt, want_lse=True, workspace=ws,
+                                                    head_wb=torch.from_numpy(wb_q).to(dev()))
+        torch.cuda.synchronize()
+        ref_o, ref_l = _per_head_reference(inp, wb_q, mode)
+        assert_close(out.cpu(), lse.cpu(), ref_o, ref_l, cfg.dtype)
+        assert torch.equal(out.cpu(), o2.cpu()) and torch.equal(lse.cpu(), l2.cpu())
