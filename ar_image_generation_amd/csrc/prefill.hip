@@ -17,7 +17,12 @@
 // transposed, O^T += V^T P^T (A = V^T by transposing LDS reads of row-major
 // V), so the online rescale is one multiply per lane register.
 //
-// Sparsity: only listed key tiles are visited.  Inside one, a wave none of
+// Sparsity: only listed key tiles are visited.  Keys below the prompt end
+// come in tiles on multiples of 64, keys past it in window tiles aligned so
+// that each 16-row block's kept run on a diagonal starts on a 16-key block
+// of the tile; a wave whose row blocks each hold their kept pairs of a tile
+// in at most two of its four 16-key blocks computes only those two (half
+// the products, exponentials and mask work of the tile).  A wave none of
 // whose rows keeps a key of the tile only takes part in the copies and
 // barriers; a wave whose blocks are all wholly kept applies no mask;
 // otherwise each row gets a 64-bit keep word over the tile's keys (causal,
@@ -110,24 +115,57 @@ __device__ inline uint64_t bit_range(int lo, int hi) {
 
 // Largest raster width the row-diagonal prefill supports: its band pattern
 // (one 64-bit word per residue mod G) lives in LDS.
-constexpr int GMAX = 1024;
+constexpr int GMAX = 1016;
 
-// Longest tile list a query tile may have (LDS copy, 8 bytes an entry):
-// sequences of up to 64 * MAX_LIST tokens.
+// Sequences of up to 64 * MAX_LIST tokens.  A query tile lists at most
+// ceil(n / 64) + 3 key tiles: prompt tiles below the prompt end, window
+// tiles from at most 15 keys before it (LDS copy, 8 bytes an entry; with
+// the ring and the band pattern a workgroup stays within 80 KiB, so two
+// share a CU).
 constexpr int MAX_LIST = 1024;
+constexpr int LIST_EXTRA = 3;
+constexpr int LIST_CAP = MAX_LIST + LIST_EXTRA;
 
-// 16-byte copy global -> LDS (global_load_lds_dwordx4; lane l's bytes land
-// at lds + 16 l).  Issued as inline assembly so that the compiler does not
-// treat it as a pending LDS write that every later LDS read must wait for:
-// the ring's own waits (vmcnt + barrier) order the stages.
-//
-// The address is a uniform 64-bit base (SGPRs) plus this lane's 32-bit byte
-// offset, so a tile's copies need no per-lane address arithmetic.
-__device__ inline void dma16(const void* sbase, uint32_t voff, const void* lds) {
-  const uint32_t dst = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds);
-  __asm__ volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(dst) : "memory");
+// A tile's copies global -> LDS (global_load_lds_dwordx4: lane l's 16
+// bytes land at M0 + 16 l), K and V alternating, DPW of each for this
+// wave.  Issued as one block of inline assembly so that the compiler does
+// not treat them as pending LDS writes that every later LDS read must wait
+// for: the ring's own waits (vmcnt + barrier) order the stages.  Each
+// address is a uniform 64-bit base (SGPRs) plus the lane's 32-bit byte
+// offset, so the copies need no per-lane address arithmetic.  The
+// compiler's hazard checks do not see inside the block, so it carries its
+// own wait states: 5 before the first copy (a VALU write of any SGPR
+// operand, 5 before a memory instruction reads it) and 1 after each M0
+// write (SALU write of M0, 1 before an LDS DMA).
+__device__ inline const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  return (const void*)(uintptr_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) << 32) |
+                                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v));
 }
+#define DA_DMA_PAIR(u)                                                        \
+  "s_mov_b32 m0, %[mk" #u "]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[k" #u "], %[kb]\n\t" \
+  "s_mov_b32 m0, %[mv" #u "]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v" #u "], %[vb]\n\t"
+template <int DPW>
+__device__ inline void dma_tile(const void* kbase, const void* vbase, const uint32_t (&ko)[DPW],
+                                const uint32_t (&vo)[DPW], uint32_t lk, uint32_t lv) {
+  static_assert(DPW == 2 || DPW == 4, "2 or 4 copies of K and of V a wave");
+  if constexpr (DPW == 4) {
+    __asm__ volatile("s_nop 4\n\t" DA_DMA_PAIR(0) DA_DMA_PAIR(1) DA_DMA_PAIR(2) DA_DMA_PAIR(3)
+                     :
+                     : [kb] "s"(kbase), [vb] "s"(vbase), [k0] "v"(ko[0]), [k1] "v"(ko[1]), [k2] "v"(ko[2]),
+                       [k3] "v"(ko[3]), [v0] "v"(vo[0]), [v1] "v"(vo[1]), [v2] "v"(vo[2]), [v3] "v"(vo[3]),
+                       [mk0] "s"(lk), [mk1] "s"(lk + 1024), [mk2] "s"(lk + 2048), [mk3] "s"(lk + 3072),
+                       [mv0] "s"(lv), [mv1] "s"(lv + 1024), [mv2] "s"(lv + 2048), [mv3] "s"(lv + 3072)
+                     : "memory", "m0");
+  } else {
+    __asm__ volatile("s_nop 4\n\t" DA_DMA_PAIR(0) DA_DMA_PAIR(1)
+                     :
+                     : [kb] "s"(kbase), [vb] "s"(vbase), [k0] "v"(ko[0]), [k1] "v"(ko[1]), [v0] "v"(vo[0]),
+                       [v1] "v"(vo[1]), [mk0] "s"(lk), [mk1] "s"(lk + 1024), [mv0] "s"(lv), [mv1] "s"(lv + 1024)
+                     : "memory", "m0");
+  }
+}
+#undef DA_DMA_PAIR
 
 // K and V tiles sit in LDS row-major with 16-byte chunk p of row r at
 // position p ^ swz(r) (common.h), so that neither the K operand reads nor
@@ -135,8 +173,22 @@ __device__ inline void dma16(const void* sbase, uint32_t voff, const void* lds) 
 
 // ---------------------------------------------------------------- tile lists
 // For query tile qt of batch b: the key tiles (BN keys) holding a kept pair,
-// in order, each with two 64-bit masks over (wave, row block, 16-key block)
-// -- bit w*8 + rb*4 + kq: that block has a kept pair / every pair is kept.
+// each with two 64-bit masks over (wave, row block, 16-key block) -- bit
+// w*8 + rb*4 + kq: that block has a kept pair / every pair is kept.  Two
+// grids of key tiles:
+//  * prompt tiles at multiples of BN, for keys below the prompt end (DENSE:
+//    every key), masked by the causal rule alone;
+//  * window tiles for keys at or past the prompt end, starting on keys
+//    congruent to i0 - B mod 16.  A 16-row block at rows r0..r0+15 keeps, on
+//    the diagonal k G of its window, the keys r0 - kG - B .. r0 - kG + 15 + B
+//    (causal: up to r0 - kG + 15), so with that alignment the run starts on a
+//    16-key block of the tile and, for B <= 8, fills at most two blocks.
+// A tile in which every row block needs at most two of the four key blocks
+// is a "half" tile: each wave computes only those two blocks per row block,
+// at half the matrix and softmax work.  The list holds the whole tiles
+// first, then the half tiles, so that the attention kernel runs them in two
+// loops (the order of the online softmax's steps does not change its
+// result beyond rounding).
 // One wave per (b, qt); lane = candidate key tile; a ballot keeps the order.
 __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
   const int lane = threadIdx.x;
@@ -146,37 +198,69 @@ __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
   const int P = clampi(a.prompt_len[b], 0, n);
   const int i0 = qt * BM_ROWS;
   const int i_last = i0 + BM_ROWS - 1 < n - 1 ? i0 + BM_ROWS - 1 : n - 1;
+  const bool dense = a.mode == DA_MODE_DENSE;
   int4* out = const_cast<int4*>(a.tile_list) + ((int64_t)b * a.n_qt + qt) * a.max_tiles * 2;
-  int count = 0;
-  const int jt_hi = i_last / BN;
-  for (int base = 0; base <= jt_hi; base += 64) {
-    const int jt = base + lane;
-    uint64_t need = 0, full = 0;
-    if (jt <= jt_hi) {
-      for (int w = 0; w < NWAVE; ++w)
-        for (int rb = 0; rb < RB_MAX; ++rb) {
-          const int rlo = i0 + (w * RB_MAX + rb) * 16;
-          if (rlo > i_last) continue;
-          const int rhi = rlo + 15 < i_last ? rlo + 15 : i_last;
-          for (int kq = 0; kq < 4; ++kq) {
-            const int jlo = jt * BN + 16 * kq;
-            const uint64_t bit = uint64_t(1) << (w * 8 + rb * 4 + kq);
-            if (range_has_kept(rlo, rhi, jlo, jlo + 15, P, a.mode, a.W, a.B, a.G)) need |= bit;
-            if (rhi == rlo + 15 && range_all_kept(rlo, jlo + 15, P, a.mode)) full |= bit;
-          }
-        }
-    }
-    const bool keep = need != 0;
-    const uint64_t bal = __ballot(keep);
-    if (keep) {
-      const int slot = count + __popcll(bal & ((uint64_t(1) << lane) - 1));
-      full &= need;
-      out[2 * slot] = make_int4(jt, (int)(uint32_t)need, (int)(uint32_t)(need >> 32), 0);
-      out[2 * slot + 1] = make_int4((int)(uint32_t)full, (int)(uint32_t)(full >> 32), 0, 0);
-    }
-    count += __popcll(bal);
+  // prompt grid: keys below pe
+  const int pe = dense ? i_last + 1 : (P < i_last + 1 ? P : i_last + 1);
+  const int n_pro = (pe + BN - 1) / BN;
+  // window grid: tiles from wb (congruent to i0 - B mod 16, at most 15
+  // before the first key past the prompt a row of the tile can keep)
+  // through the last row
+  int n_win = 0, wb = 0;
+  if (!dense) {
+    const int reach = a.mode == DA_MODE_BAND ? (a.B < a.W ? a.B : a.W) : a.W;
+    const int wlo = i0 - reach > P ? i0 - reach : P;
+    wb = wlo - ((wlo - (i0 - a.B)) & 15);
+    n_win = wlo <= i_last ? (i_last - wb) / BN + 1 : 0;
   }
-  if (lane == 0) const_cast<int32_t*>(a.tile_count)[(int64_t)b * a.n_qt + qt] = count;
+  int count = 0, n_whole = 0;
+  for (int pass = 0; pass < 2; ++pass) {        // whole tiles, then half tiles
+    for (int base = 0; base < n_pro + n_win; base += 64) {
+      const int c = base + lane;
+      const bool win = c >= n_pro;
+      const int j0 = win ? wb + (c - n_pro) * BN : c * BN;
+      uint64_t need = 0, full = 0;
+      bool half = true;                          // every row block needs <= 2 key blocks
+      if (c < n_pro + n_win) {
+        for (int w = 0; w < NWAVE; ++w)
+          for (int rb = 0; rb < RB_MAX; ++rb) {
+            const int rlo = i0 + (w * RB_MAX + rb) * 16;
+            if (rlo > i_last) continue;
+            const int rhi = rlo + 15 < i_last ? rlo + 15 : i_last;
+            int nk = 0;
+            for (int kq = 0; kq < 4; ++kq) {
+              const int jlo = j0 + 16 * kq, jhi = jlo + 15;
+              const uint64_t bit = uint64_t(1) << (w * 8 + rb * 4 + kq);
+              bool has, all;
+              if (!win) {
+                has = jlo <= rhi && (dense || jlo < P);
+                all = rhi == rlo + 15 && jhi <= rlo && (dense || jhi < P);
+              } else {
+                const int jl = jlo > P ? jlo : P;
+                has = jl <= jhi && range_has_kept(rlo, rhi, jl, jhi, P, a.mode, a.W, a.B, a.G);
+                all = false;
+              }
+              if (has) { need |= bit; ++nk; }
+              if (all) full |= bit;
+            }
+            half = half && nk <= 2;
+          }
+      }
+      const bool keep = need != 0 && half == (pass == 1);
+      const uint64_t bal = __ballot(keep);
+      const int slot = count + __popcll(bal & ((uint64_t(1) << lane) - 1));
+      if (keep && slot < a.max_tiles) {
+        full &= need;
+        out[2 * slot] = make_int4(j0, (int)(uint32_t)need, (int)(uint32_t)(need >> 32), win ? 1 : 0);
+        out[2 * slot + 1] = make_int4((int)(uint32_t)full, (int)(uint32_t)(full >> 32), 0, 0);
+      }
+      count += __popcll(bal);
+    }
+    if (pass == 0) n_whole = count;
+  }
+  count = count < a.max_tiles ? count : a.max_tiles;
+  n_whole = n_whole < count ? n_whole : count;
+  if (lane == 0) const_cast<int32_t*>(a.tile_count)[(int64_t)b * a.n_qt + qt] = count | (n_whole << 16);
 }
 
 // ---------------------------------------------------------------- attention
@@ -198,10 +282,11 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   // before a query at residue r (mod G) lies within B of a multiple of G
   __shared__ uint64_t bp[MODE == DA_MODE_ROWDIAG ? GMAX : 1];
   // this query tile's list, read from LDS so that no list read waits behind
-  // the tile DMA in flight: x = key tile | (wave w's blocks all wholly kept)
-  // << (16 + w), y = the need bits (8 per wave: row block rb, key block kq at
-  // bit 8w + 4rb + kq -- the block holds a kept pair)
-  __shared__ int2 tl[MAX_LIST];
+  // the tile DMA in flight: x = (first key + 16) | window tile << 17 |
+  // (wave w's blocks all wholly kept) << (18 + w), y = the need bits (8 per
+  // wave: row block rb, key block kq at bit 8w + 4rb + kq -- the block holds
+  // a kept pair)
+  __shared__ int2 tl[LIST_CAP];
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches
@@ -220,24 +305,48 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   const int hk = h / (a.heads / a.kv_heads);
   const int i0 = qt * BM_ROWS;
   const int n = a.n;
-  const int P = clampi(a.prompt_len[b], 0, n);
   const int i_last = i0 + BM_ROWS - 1 < n - 1 ? i0 + BM_ROWS - 1 : n - 1;
   const int W = a.W, Bw = a.B, G = a.G;
-  const int jt_max = (n - 1) / BN;
 
   const int64_t lid = (int64_t)b * a.n_qt + qt;
-  const int cnt = clampi(a.tile_count[lid], 0, a.max_tiles);
   const int4* list = a.tile_list + lid * a.max_tiles * 2;
+  // one round trip before the first tile's copies: the list length (and
+  // its number of whole tiles, listed first), its first entry and this
+  // thread's entry, the prompt length
+  const int cw = __builtin_amdgcn_readfirstlane(a.tile_count[lid]);   // uniform loop bounds
+  const int cnt = clampi(cw & 0xffff, 0, a.max_tiles);
+  const int n_whole = clampi((int)((uint32_t)cw >> 16), 0, cnt);
+  const int4 first = list[0];
+  int4 mine0 = make_int4(0, 0, 0, 0), mine1 = make_int4(0, 0, 0, 0);
+  if (t < a.max_tiles) {
+    mine0 = list[2 * t];
+    mine1 = list[2 * t + 1];
+  }
+  const int P = clampi(a.prompt_len[b], 0, n);
 
   const uint16_t* qb = a.q + b * a.sq[0] + h * a.sq[1];
-  const uint16_t* kb = a.k + b * a.sk[0] + hk * a.sk[1];
-  const uint16_t* vb = a.v + b * a.sv[0] + hk * a.sv[1];
+  const uint16_t* kb = (const uint16_t*)uniform_ptr(a.k + b * a.sk[0] + hk * a.sk[1]);
+  const uint16_t* vb = (const uint16_t*)uniform_ptr(a.v + b * a.sv[0] + hk * a.sv[1]);
 
-  // DMA of key tile jt into ring stage st: this wave's DPW transfers of K
-  // and of V; lane l of transfer u fills LDS chunk l of its 1 KiB block.
-  // This lane's row of each transfer and its byte offsets from the tile's
-  // first row (fixed per lane; under 4 GiB, checked on the host); in the
-  // last tile, rows past the end read the last row instead
+  // ---- this wave's 16*RB query rows; lane lr of block rb holds row
+  // wi0 + 16*rb + lr; its Q^T operand chunks stay in registers
+  const int wi0 = i0 + wave * 16 * RB;
+  bf16x8 qv[RB][NC];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int i = wi0 + 16 * rb + lr;
+    const uint16_t* qrow = qb + (int64_t)(i < n ? i : n - 1) * a.sq[2];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      qv[rb][c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + lg * 8);
+  }
+
+  // DMA of the key tile starting at key j0 into ring stage st: this wave's
+  // DPW transfers of K and of V; lane l of transfer u fills LDS chunk l of
+  // its 1 KiB block.  This lane's row of each transfer and its byte offsets
+  // from the tile's first row (fixed per lane; under 4 GiB, checked on the
+  // host); rows before key 0 or past the last key read the nearest key
+  // instead (no mask keeps them)
   int dma_row[DPW], dma_c8[DPW];
   uint32_t dko[DPW], dvo[DPW];
 #pragma unroll
@@ -250,42 +359,37 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
     dko[u] = (uint32_t)(((int64_t)row * a.sk[2] + chunk * 8) * 2);
     dvo[u] = (uint32_t)(((int64_t)row * a.sv[2] + chunk * 8) * 2);
   }
-  auto issue = [&](int jt, int st) {
-    jt = __builtin_amdgcn_readfirstlane(clampi(jt, 0, jt_max));
-    uint16_t* kd = ring + st * 2 * TILE;
-    uint16_t* vd = kd + TILE;
-    const int j0 = jt * BN;
-    const uint16_t* ks = kb + (int64_t)j0 * a.sk[2];
-    const uint16_t* vs = vb + (int64_t)j0 * a.sv[2];
-    if (j0 + BN <= n) {
-#pragma unroll
-      for (int u = 0; u < DPW; ++u) {
-        const int blk = wave * DPW + u;
-        dma16(ks, dko[u], kd + blk * 512);
-        dma16(vs, dvo[u], vd + blk * 512);
-      }
+  // LDS byte address of this wave's first 1 KiB block of ring stage 0 (K)
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring) + wave * DPW * 1024;
+  auto issue = [&](int j0, int st) __attribute__((always_inline)) {
+    j0 = __builtin_amdgcn_readfirstlane(j0);
+    const uint32_t lk = lds0 + st * 2 * TILE * 2, lv = lk + TILE * 2;
+    if (j0 >= 0 && j0 + BN <= n) {
+      dma_tile<DPW>(kb + (int64_t)j0 * a.sk[2], vb + (int64_t)j0 * a.sv[2], dko, dvo, lk, lv);
     } else {
+      const int jb = j0 > 0 ? j0 : 0;                 // j0 <= n - 1
+      uint32_t ko[DPW], vo[DPW];
 #pragma unroll
       for (int u = 0; u < DPW; ++u) {
-        const int blk = wave * DPW + u;
-        const int r = j0 + dma_row[u] < n ? dma_row[u] : n - 1 - j0;
-        dma16(ks, (uint32_t)(((int64_t)r * a.sk[2] + dma_c8[u]) * 2), kd + blk * 512);
-        dma16(vs, (uint32_t)(((int64_t)r * a.sv[2] + dma_c8[u]) * 2), vd + blk * 512);
+        const int r = clampi(j0 + dma_row[u], 0, n - 1) - jb;   // 0 .. 63
+        ko[u] = (uint32_t)(((int64_t)r * a.sk[2] + dma_c8[u]) * 2);
+        vo[u] = (uint32_t)(((int64_t)r * a.sv[2] + dma_c8[u]) * 2);
       }
+      dma_tile<DPW>(kb + (int64_t)jb * a.sk[2], vb + (int64_t)jb * a.sv[2], ko, vo, lk, lv);
     }
   };
+  auto entry_j0 = [&](int x) { return clampi(x, -15, n - 1); };
+  if (cnt > 0) issue(entry_j0(__builtin_amdgcn_readfirstlane(first.x)), 0);
 
-  for (int e = t; e < cnt; e += NTHREADS) {
-    const int4 e0 = list[2 * e];
-    const int4 e1 = list[2 * e + 1];
+  auto pack = [&](int4 e0, int4 e1) {
     int allfull = 0;
 #pragma unroll
     for (int w = 0; w < NWAVE; ++w) allfull |= (((uint32_t)e1.x >> (8 * w)) & 0xffu) == 0xffu ? 1 << w : 0;
-    tl[e] = make_int2(clampi(e0.x, 0, jt_max) | (allfull << 16), e0.y);
-  }
-  __syncthreads();
-
-  issue(tl[0].x & 0xffff, 0);
+    return make_int2((entry_j0(e0.x) + 16) | ((e0.w & 1) << 17) | (allfull << 18), e0.y);
+  };
+  if (t < cnt) tl[t] = pack(mine0, mine1);
+  for (int e = t + NTHREADS; e < cnt; e += NTHREADS) tl[e] = pack(list[2 * e], list[2 * e + 1]);
 
   if constexpr (MODE == DA_MODE_ROWDIAG) {
     // band centres of residue r within reach of bits 0..63: r - kG for
@@ -303,19 +407,6 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
     }
   }
 
-  // ---- this wave's 16*RB query rows; lane lr of block rb holds row
-  // wi0 + 16*rb + lr; its Q^T operand chunks stay in registers
-  const int wi0 = i0 + wave * 16 * RB;
-  bf16x8 qv[RB][NC];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int i = wi0 + 16 * rb + lr;
-    const uint16_t* qrow = qb + (int64_t)(i < n ? i : n - 1) * a.sq[2];
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-      qv[rb][c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + lg * 8);
-  }
-
   float mq[RB], ls[RB];                // running reference max (scaled), partial sum
   f32x4 o[RB][NB];
 #pragma unroll
@@ -330,87 +421,65 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   const int vt_sub = (lr & 3);
   const int my_i0 = wi0 + lr;          // this lane's row in block 0 (block rb adds 16 rb)
 
-  // Masks: a 64-bit keep word per row over the keys of the tile whose first
-  // key is j0 -- causal bits, prompt bits and the window rule -- applied to
-  // that tile's four 16-key score blocks: each score the lane holds
-  // (key 16kq + 4lg + r) keeps its bit or becomes -inf.
-  auto apply_mask = [&](f32x4 (&sc)[RB][4], int j0) {
-    // a tile wholly past the prompt, below every row's diagonal and inside
-    // every row's window needs only the band pattern (uniform per wave)
-    const bool inner = MODE == DA_MODE_ROWDIAG && j0 >= P && wi0 - j0 >= BN - 1 &&
-                       wi0 + 16 * RB - 1 - j0 <= W;
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const int x = my_i0 + 16 * rb - j0;
-      uint64_t keep;
-      if (inner) {
-        keep = bp[mod_g(x, G, a.inv_g)];
-      } else {
-        uint64_t win;
-        if constexpr (MODE == DA_MODE_ROWDIAG) win = bp[mod_g(x, G, a.inv_g)] & bit_range(x - W, x);
-        else if constexpr (MODE == DA_MODE_BAND) win = bit_range(x - (Bw < W ? Bw : W), x);
-        else win = ~uint64_t(0);
-        keep = (win | bit_range(0, P - j0 - 1)) & bit_range(0, x);
-      }
-      const uint64_t sh = keep >> (4 * lg);
-      const uint32_t wd[2] = {(uint32_t)sh, (uint32_t)(sh >> 32)};
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int32_t m = (int32_t)(wd[kq >> 1] << (31 - (16 * (kq & 1) + r))) >> 31;
-          sc[rb][kq][r] = __int_as_float((__float_as_int(sc[rb][kq][r]) & m) | (~m & (int32_t)0xff800000));
-        }
+  // Keep word of this lane's row in block rb over the tile's keys j0..j0+63
+  // (bit c: key j0 + c at distance x - c).  Prompt tiles: the causal bits
+  // (and below the prompt end); window tiles: the window rule at or past
+  // the prompt end.  A window tile past the prompt, below every row's
+  // diagonal and inside every row's window needs only the band pattern.
+  auto keep_word = [&](int rb, int j0, bool win, bool inner) __attribute__((always_inline)) -> uint64_t {
+    const int x = my_i0 + 16 * rb - j0;
+    if (!win) {
+      if constexpr (MODE == DA_MODE_DENSE) return bit_range(0, x);
+      else return bit_range(0, (x < P - j0 - 1 ? x : P - j0 - 1));
+    }
+    if constexpr (MODE == DA_MODE_ROWDIAG) {
+      const uint64_t band = bp[mod_g(x, G, a.inv_g)];
+      return inner ? band : band & bit_range(x - W, x) & bit_range(P - j0, 63);
+    } else {
+      return bit_range(x - (Bw < W ? Bw : W), x) & bit_range(P - j0, 63);
     }
   };
-  // S^T = K Q^T for the four 16-key blocks of one staged tile (A = K from
-  // LDS, shared by the RB row blocks)
-  auto scores_into = [&](const uint16_t* ksm, f32x4 (&sc)[RB][4]) {
+
+  // One step over NQ of the staged tile's 16-key blocks per row block:
+  // blk[rb][..] (all four, or the two holding row block rb's kept pairs).
+  // S^T = K Q^T (A = K from LDS), masks, online softmax, O^T += V^T P^T
+  // over pairs of blocks (A = V^T by transposing LDS reads).  Rows 16
+  // apart share the swizzle, so a block's LDS addresses are a per-lane base
+  // plus 16 q rows.
+  auto body = [&](auto nq, const uint16_t* st0, const int (&blk)[RB][4], bool masked, int j0, bool win,
+                  bool inner) __attribute__((always_inline)) {
+    constexpr int NQ = decltype(nq)::value;
+    f32x4 sc[RB][NQ];
 #pragma unroll
-    for (int kq = 0; kq < 4; ++kq) {
+    for (int hq = 0; hq < NQ; ++hq) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sc[rb][kq] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int row = 16 * kq + lr;
+      for (int rb = 0; rb < RB; ++rb) sc[rb][hq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const int pos = (4 * c + lg) ^ swz<CPR>(row);
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(ksm + row * HD + pos * 8);
+        const int pos = (4 * c + lg) ^ swz<CPR>(lr);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          sc[rb][kq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][kq], 0, 0, 0);
+        for (int rb = 0; rb < RB; ++rb) {
+          const int row = 16 * blk[rb][hq] + lr;
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st0 + row * HD + pos * 8);
+          sc[rb][hq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][hq], 0, 0, 0);
+        }
       }
     }
-  };
-
-  // One listed tile a step, tile t in stage t % NS.  At the top of step idx
-  // tile idx has landed and every wave is done with step idx-1, whose stage
-  // then receives tile idx+1 -- fetched while this step computes.  The
-  // DMA is invisible to the compiler's waits: each wave waits for its own
-  // part (vmcnt), then the barrier covers every wave's part.
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-  __syncthreads();                     // tile 0 landed, band pattern written
-  // the step body takes its ring stage as a constant (the loop runs two
-  // steps an iteration), so every LDS address is a fixed per-lane base
-  // plus an immediate offset
-  auto step = [&](int idx, auto stage) {
-    constexpr int ST = decltype(stage)::value;
-    if (idx > 0) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // tile idx (this wave's part)
-      __builtin_amdgcn_s_barrier();               // everyone's part; step idx-1 done
-      __asm__ volatile("" ::: "memory");
+    if (masked) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const uint64_t keep = keep_word(rb, j0, win, inner);
+#pragma unroll
+        for (int hq = 0; hq < NQ; ++hq) {
+          const uint32_t wd = (uint32_t)(keep >> (16 * blk[rb][hq] + 4 * lg));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int32_t m = (int32_t)(wd << (31 - r)) >> 31;
+            sc[rb][hq][r] = __int_as_float((__float_as_int(sc[rb][hq][r]) & m) | (~m & (int32_t)0xff800000));
+          }
+        }
+      }
     }
-    if (idx + 1 < cnt) issue(tl[idx + 1].x & 0xffff, (ST + 1) % NS);
-    const int2 e0 = tl[idx];
-    const unsigned need8 = ((uint32_t)e0.y >> (wave * 8)) & 0xffu;
-    // a wave without a kept pair in this tile only takes part in the copies
-    // and barriers
-    if (need8 == 0) return;
-    const bool allfull = (e0.x >> (16 + wave)) & 1;
-    const uint16_t* st0 = ring + ST * 2 * TILE;
-
-    f32x4 sc[RB][4];
-    scores_into(st0, sc);
-    if (!allfull) apply_mask(sc, (e0.x & 0xffff) * BN);
 
     float mts[RB];
     bool grow = false;
@@ -418,9 +487,9 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
     for (int rb = 0; rb < RB; ++rb) {
       float mt = -INFINITY;
 #pragma unroll
-      for (int kq = 0; kq < 4; ++kq)
+      for (int hq = 0; hq < NQ; ++hq)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[rb][kq][r]);
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, sc[rb][hq][r]);
       mts[rb] = max_over_row_groups(mt) * a.qscale;
       grow = grow || mts[rb] > mq[rb] + 8.f;
     }
@@ -437,12 +506,12 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
         mq[rb] = mn;
       }
     }
-    bf16x8 pb[RB][2];                // P^T of the tile's two 32-key chunks
+    bf16x8 pb[RB][NQ / 2];           // P^T of the step's 32-key pairs of blocks
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const float mref = mq[rb] == -INFINITY ? 0.f : mq[rb];
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+      for (int cc = 0; cc < NQ / 2; ++cc)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = __builtin_amdgcn_exp2f(fmaf(sc[rb][2 * cc + e / 4][e % 4], a.qscale, -mref));
@@ -450,33 +519,98 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
           pb[rb][cc][e] = (__bf16)p;
         }
     }
-    // O^T += V^T P^T over the tile's two 32-key chunks
-    const uint16_t* vsm = st0 + TILE;
+    // O^T += V^T P^T: the pair's blocks give the product's 32 keys
 #pragma unroll
-    for (int ch = 0; ch < 2; ++ch) {
+    for (int cc = 0; cc < NQ / 2; ++cc) {
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         typedef short v4i16 __attribute__((ext_vector_type(4)));
-        const int chunk = 2 * nb + (vt_sub >> 1);
-        const int r_lo = 32 * ch + vt_row, r_hi = r_lo + 16;
-        const uint16_t* plo = vsm + r_lo * HD + ((chunk ^ swz<CPR>(r_lo)) * 8) + (vt_sub & 1) * 4;
-        const uint16_t* phi = vsm + r_hi * HD + ((chunk ^ swz<CPR>(r_hi)) * 8) + (vt_sub & 1) * 4;
-        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
         typedef short v8i16 __attribute__((ext_vector_type(8)));
-        const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+        const int chunk = 2 * nb + (vt_sub >> 1);
+        const int lane_off = vt_row * HD + ((chunk ^ swz<CPR>(vt_row)) * 8) + (vt_sub & 1) * 4;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][ch], o[rb][nb], 0, 0, 0);
+        for (int rb = 0; rb < RB; ++rb) {
+          const uint16_t* plo = st0 + TILE + 16 * blk[rb][2 * cc] * HD + lane_off;
+          const uint16_t* phi = st0 + TILE + 16 * blk[rb][2 * cc + 1] * HD + lane_off;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
+          const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+          o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][cc], o[rb][nb], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // One listed tile a step, tile t in stage t % NS.  At the top of step idx
+  // tile idx has landed and every wave is done with step idx-1, whose stage
+  // then receives tile idx+1 -- fetched while this step computes.  The
+  // DMA is invisible to the compiler's waits: each wave waits for its own
+  // part (vmcnt), then the barrier covers every wave's part.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();                     // tile 0 landed, list and band pattern written
+  // the step body takes its ring stage as a constant (the loop runs two
+  // steps an iteration), so every LDS address is a fixed per-lane base
+  // plus an immediate offset
+  auto step = [&](int idx, auto stage, auto nq) __attribute__((always_inline)) {
+    constexpr int ST = decltype(stage)::value;
+    constexpr int NQ = decltype(nq)::value;
+    if (idx > 0) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // tile idx (this wave's part)
+      __builtin_amdgcn_s_barrier();               // everyone's part; step idx-1 done
+      __asm__ volatile("" ::: "memory");
+    }
+    if (idx + 1 < cnt) issue((tl[idx + 1].x & 0x1ffff) - 16, (ST + 1) % NS);
+    const int2 e = tl[idx];
+    const int ex = __builtin_amdgcn_readfirstlane(e.x);
+    const unsigned need8 = ((uint32_t)__builtin_amdgcn_readfirstlane(e.y) >> (wave * 8)) & 0xffu;
+    // a wave without a kept pair in this tile only takes part in the copies
+    // and barriers
+    if (need8 == 0) return;
+    const int j0 = (ex & 0x1ffff) - 16;
+    const bool win = (ex >> 17) & 1;
+    const uint16_t* st0 = ring + ST * 2 * TILE;
+    const bool inner = MODE == DA_MODE_ROWDIAG && win && j0 >= P && wi0 - j0 >= BN - 1 &&
+                       wi0 + 16 * RB - 1 - j0 <= W;
+    if constexpr (NQ == 2) {
+      // each row block's (at most) two key blocks holding its kept pairs; a
+      // row block with one takes a second it has no kept pair in
+      int blk[RB][4];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const unsigned m4 = (need8 >> (4 * rb)) & 0xfu;
+        const int q0 = m4 ? __builtin_ctz(m4) : 0;
+        const unsigned rest = m4 & (m4 - 1);
+        blk[rb][0] = q0;
+        blk[rb][1] = rest ? __builtin_ctz(rest) : (q0 + 1) & 3;
+        blk[rb][2] = blk[rb][3] = 0;
+      }
+      body(nq, st0, blk, true, j0, win, inner);
+    } else {
+      const int blk[RB][4] = {{0, 1, 2, 3}, {0, 1, 2, 3}};
+      const bool allfull = (ex >> (18 + wave)) & 1;
+      body(nq, st0, blk, !allfull, j0, win, inner);
+    }
+  };
+  // tiles from..to-1 (all whole or all half), tile idx in ring stage idx % 2
+  auto run = [&](auto nq, int from, int to) __attribute__((always_inline)) {
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    if (from & 1) {
+      for (int idx = from; idx < to; idx += 2) {
+        step(idx, S1{}, nq);
+        if (idx + 1 < to) step(idx + 1, S0{}, nq);
+      }
+    } else {
+      for (int idx = from; idx < to; idx += 2) {
+        step(idx, S0{}, nq);
+        if (idx + 1 < to) step(idx + 1, S1{}, nq);
       }
     }
   };
   static_assert(NS == 2, "two steps an iteration, one per stage");
-  for (int idx = 0; idx < cnt; idx += 2) {
-    step(idx, std::integral_constant<int, 0>{});
-    if (idx + 1 < cnt) step(idx + 1, std::integral_constant<int, 1>{});
-  }
+  run(std::integral_constant<int, 4>{}, 0, n_whole);
+  run(std::integral_constant<int, 2>{}, n_whole, cnt);
 
   // ---- normalise and store: lane holds row wi0+16rb+lr, dims 16nb + 4lg + r
 #pragma unroll
@@ -497,14 +631,12 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
       a.lse[((int64_t)b * a.heads + h) * n + i] = (mq[rb] + log2f(L)) * kLn2P;
   }
 }
-
-
 }  // namespace da
 
 using namespace da;
 
 static int n_query_tiles(int n) { return (n + BM_ROWS - 1) / BM_ROWS; }
-static int max_key_tiles(int n) { return (n + BN - 1) / BN; }
+static int max_key_tiles(int n) { return (n + BN - 1) / BN + LIST_EXTRA; }
 
 extern "C" int64_t da_prefill_tiles_bytes(int32_t batch, int32_t n) {
   if (batch < 0 || n < 0) return fail(DA_EINVAL, "batch=%d n=%d", batch, n);

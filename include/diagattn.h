@@ -345,18 +345,28 @@ int64_t da_prefill_tiles_bytes(int32_t batch, int32_t n);
 /* prefill_tiles_build -- the tile lists of the keep-set for prefill.
  *
  * Queries are cut into tiles of 128 rows (4 waves x 2 blocks of 16) and keys
- * into tiles of 64 (4 blocks of 16).  For each batch b and query tile qt
- * this writes, in key order, the key tiles that hold at least one kept
- * (row, key) pair of the causal keep rule (prompt_len[b] prompt tokens), and
- * for each two 64-bit masks over (wave w, row block rb, key block kq), bit
- * w*8 + rb*4 + kq: the block holds a kept pair / every pair of the block is
- * kept (bits 32..63, waves 4..7, are zero with 4 waves a tile).  Layout of `tiles` (16-byte aligned, da_prefill_tiles_bytes long):
- *   int32 count[batch][n_qt], padded to 16 bytes, then
- *   int32 entry[batch][n_qt][max_tiles][8] = {key tile, need lo, need hi, 0,
- *                                             full lo, full hi, 0, 0}
- * with n_qt = ceil(n / 128), max_tiles = ceil(n / 64).  The lists depend only
- * on the mask, n and prompt_len: build them once and reuse them for every
- * head and layer.
+ * into tiles of 64 (4 blocks of 16) on two grids: prompt tiles at multiples
+ * of 64 for keys below prompt_len[b] (DENSE: every key), and window tiles
+ * for keys at or past it, starting on keys congruent to (first row - B)
+ * mod 16, so that the kept keys of a 16-row block on one diagonal of the
+ * row-diagonal rule (summary page, core formulas) start on a 16-key block.
+ * For each batch b and query tile qt this writes the key tiles that hold at
+ * least one kept (row, key) pair of the causal keep rule -- prompt tiles
+ * counting keys below the prompt end only, window tiles keys at or past it
+ * -- and for each two 64-bit masks over (wave w, row block rb, key block kq),
+ * bit w*8 + rb*4 + kq: the block holds a kept pair / every pair of the block
+ * is kept (bits 32..63, waves 4..7, are zero with 4 waves a tile).  Tiles in
+ * which some row block needs three or four of the key blocks come first
+ * ("whole" tiles), then the tiles in which every row block needs at most two
+ * ("half" tiles: only those two are computed).  Layout of `tiles` (16-byte
+ * aligned, da_prefill_tiles_bytes long):
+ *   int32 count[batch][n_qt] = list length | number of whole tiles << 16,
+ *         padded to 16 bytes, then
+ *   int32 entry[batch][n_qt][max_tiles][8] = {first key, need lo, need hi,
+ *         window tile (0/1), full lo, full hi, 0, 0}
+ * with n_qt = ceil(n / 128), max_tiles = ceil(n / 64) + 3; a window tile's
+ * first key may be up to 15 below 0.  The lists depend only on the mask, n
+ * and prompt_len: build them once and reuse them for every head and layer.
  * Errors: DA_EINVAL (mask, sizes, null pointers, alignment), DA_ENOTSUP
  * (causal = 0), DA_ECAPACITY (tiles_bytes too small). */
 int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t n,
@@ -393,13 +403,13 @@ int da_prefill_tiles_build(const da_mask* m /* [host] */, int32_t batch, int32_t
  * and counts are clamped into range, so an inconsistent list gives wrong
  * numbers, never an out-of-bounds access.
  * Limits (LDS copies of the tile list and of the row-diagonal band pattern):
- * n <= 65536 tokens; in ROWDIAG mode G <= 1024; the k and v position strides
+ * n <= 65536 tokens; in ROWDIAG mode G <= 1016; the k and v position strides
  * such that 63 positions plus one row span under 4 GiB (32-bit offsets
  * within a 64-key tile).
  * Errors: DA_EINVAL (mask, null pointers, sizes, strides, alignment, a
  * scale that is not positive and finite),
  * DA_ENOTSUP (causal = 0, dtype other than bf16, head_dim not 64/128,
- * n > 65536, ROWDIAG with G > 1024, k/v position stride too large),
+ * n > 65536, ROWDIAG with G > 1016, k/v position stride too large),
  * DA_ECAPACITY (tiles_bytes below da_prefill_tiles_bytes(batch, n)). */
 int da_band_prefill_attn(const da_mask* m /* [host] */, da_dtype dtype, int32_t batch,
                          int32_t heads, int32_t kv_heads, int32_t n, int32_t head_dim,

@@ -202,3 +202,63 @@ def test_window_and_band_at_the_int32_limit(W, B, G):
         out, lse = run(q, k, v, prompt, mode, W, B, G)
         rows = [(b, h, i) for b in range(2) for h in range(2) for i in range(n)]
         check(out, lse, oracle_rows(q, k, v, prompt, mode, Wr, Br, G, rows))
+
+
+def _parse_tiles(tiles, batch, n):
+    n_qt = (n + 127) // 128
+    max_tiles = (n + 63) // 64 + 3
+    raw = tiles.cpu().numpy().view(np.int32)
+    counts = raw[:batch * n_qt].reshape(batch, n_qt)
+    off = ((batch * n_qt * 4 + 15) // 16 * 16) // 4
+    ent = raw[off:off + batch * n_qt * max_tiles * 8].reshape(batch, n_qt, max_tiles, 8)
+    return counts, ent, max_tiles
+
+
+@pytest.mark.parametrize("mode,n,P,W,B,G", [(O.ROWDIAG, 600, 256, 256, 3, 64), (O.ROWDIAG, 300, 17, 96, 2, 32),
+                                            (O.ROWDIAG, 283, 3, 64, 3, 16), (O.BAND, 283, 20, 64, 3, 16),
+                                            (O.DENSE, 283, 20, 64, 3, 16), (O.ROWDIAG, 130, 7, 40, 9, 10),
+                                            (O.ROWDIAG, 700, 31, 2**31 - 1, 8, 64)])
+def test_tile_lists_hold_every_kept_pair_once(mode, n, P, W, B, G):
+    """The prefill tile lists against the oracle's keep rule: every kept
+    (row, key) pair lies in exactly one listed (tile, 16-key block) marked as
+    holding a kept pair -- prompt tiles counting keys below the prompt end,
+    window tiles keys at or past it -- every block marked wholly kept is, in
+    a half tile each row block marks at most two blocks, and whole tiles come
+    first."""
+    prompt = [P, min(P, n) // 2]
+    m = da.mask(mode, W, B, G)
+    tiles = da.prefill_tiles_build(m, torch.as_tensor(prompt, dtype=torch.int32).to(DEV), n)
+    torch.cuda.synchronize()
+    counts, ent, max_tiles = _parse_tiles(tiles, len(prompt), n)
+    for b, Pb in enumerate(prompt):
+        Pc = min(Pb, n)
+        keep = np.stack([O.keep_row(i, n, P=Pc, W=min(W, n), B=min(B, n), G=G, mode=mode) for i in range(n)])
+        seen = np.zeros((n, n), dtype=np.int32)
+        for qt in range(counts.shape[1]):
+            cnt, n_whole = int(counts[b, qt]) & 0xffff, int(counts[b, qt]) >> 16
+            assert 0 < cnt <= max_tiles and n_whole <= cnt
+            i0 = 128 * qt
+            for e in range(cnt):
+                j0, nlo, nhi, win, flo, fhi = (int(x) for x in ent[b, qt, e, :6])
+                need = (nlo & 0xffffffff) | ((nhi & 0xffffffff) << 32)
+                full = (flo & 0xffffffff) | ((fhi & 0xffffffff) << 32)
+                assert -15 <= j0 < n and need != 0
+                for w in range(4):
+                    for rb in range(2):
+                        r0 = i0 + 32 * w + 16 * rb
+                        bits = (need >> (8 * w + 4 * rb)) & 0xf
+                        if e >= n_whole:
+                            assert bin(bits).count("1") <= 2, (b, qt, e, w, rb)
+                        for kq in range(4):
+                            if not (bits >> kq) & 1:
+                                continue
+                            jl = j0 + 16 * kq
+                            for i in range(r0, min(r0 + 16, n)):
+                                js = np.arange(max(jl, 0), min(jl + 16, n))
+                                js = js[(js >= Pc) if win else (js < Pc) if mode != O.DENSE else js >= 0]
+                                kept = keep[i, js]
+                                seen[i, js[kept]] += 1
+                                if (full >> (8 * w + 4 * rb + kq)) & 1:
+                                    assert kept.all() and len(js) == 16
+        assert np.array_equal(seen > 0, keep), b
+        assert seen.max() <= 1, b
