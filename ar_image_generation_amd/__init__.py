@@ -11,11 +11,13 @@ from .api import (  # noqa: F401
     decode_schedule,
     decode_workspace,
     decode_workspace_bytes,
+    gather_read_probe,
     hbm_read_probe,
     keep_cap,
     keep_count,
     keepset_build,
     keepset_tiles,
+    kept_row_offsets,
     kv_cache,
     mask,
     prefill_tiles_build,

@@ -36,6 +36,7 @@ SIGNATURES = {
                                         c_i64, c_vp, c_vp]),
     "da_decode_workspace_bytes": (c_i64, [c_i32, c_i32, c_i32, c_i32, c_i32]),
     "da_hbm_read_probe": (ctypes.c_int, [c_vp, c_i64, c_vp, c_i32, c_i32, c_vp]),
+    "da_gather_read_probe": (ctypes.c_int, [c_vp, c_vp, c_vp, c_i64, c_i32, c_i64, c_vp, c_i32, c_i32, c_vp]),
     "da_prefill_tiles_bytes": (c_i64, [c_i32, c_i32]),
     "da_prefill_tiles_build": (ctypes.c_int, [ctypes.POINTER(DaMask), c_i32, c_i32, c_vp, c_vp,
                                               c_i64, c_vp]),

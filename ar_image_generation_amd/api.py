@@ -371,6 +371,51 @@ def hbm_read_probe(buf: torch.Tensor, sink: torch.Tensor, grid: int,
           "da_hbm_read_probe")
 
 
+def kept_row_offsets(k_cache: torch.Tensor, seq: torch.Tensor, count: torch.Tensor, idx: torch.Tensor,
+                     block_table: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Byte offsets (int64, device) from the cache's base of the K (and V)
+    rows a decode step keeps: every kv head of every listed entry of the
+    per-query lists count [n_q], idx [n_q, cap], in (query, kv head, entry)
+    order, addressed as ``kv_cache`` describes the cache.  Measurement
+    set-up for ``gather_read_probe``, computed with torch ops."""
+    kv = kv_cache(k_cache, k_cache, block_table)
+    esz = k_cache.element_size()
+    n_q, cap = idx.shape
+    hkv = k_cache.shape[1]
+    dev = idx.device
+    valid = torch.arange(cap, device=dev)[None, :] < count.long()[:, None]
+    j = idx.long().clamp(0, kv.max_len - 1)
+    sq = seq.long()[:, None]
+    if block_table is not None:
+        page = block_table.long()[sq.clamp(0, kv.n_seq - 1), j // kv.page_size].clamp(0, kv.n_pages - 1)
+        row = page * kv.page_stride + (j % kv.page_size) * kv.slot_stride
+    else:
+        row = sq.clamp(0, kv.n_pages - 1) * kv.page_stride + j * kv.slot_stride
+    off = row[:, None, :] + torch.arange(hkv, device=dev)[None, :, None] * kv.head_stride
+    return (off[valid[:, None, :].expand(n_q, hkv, cap)] * esz).contiguous()
+
+
+def gather_read_probe(k_cache: torch.Tensor, v_cache: torch.Tensor, offsets: torch.Tensor,
+                      sink: torch.Tensor, grid: int, *, loads_in_flight: int = 2) -> None:
+    """Reads the K and V rows at the byte ``offsets`` (``kept_row_offsets``)
+    and nothing else (measurement); sink [grid] int32 receives one XOR a
+    workgroup."""
+    _need_cuda("gather_read_probe", k_cache, v_cache, offsets, sink)
+    if k_cache.shape != v_cache.shape or k_cache.dtype != v_cache.dtype or \
+            not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("gather_read_probe: k and v must be contiguous and alike")
+    if offsets.dtype != torch.int64 or not offsets.is_contiguous():
+        raise ValueError("gather_read_probe: offsets must be contiguous int64")
+    if sink.numel() < grid or sink.element_size() != 4:
+        raise ValueError("gather_read_probe: sink needs grid 32-bit words")
+    row_bytes = k_cache.shape[-1] * k_cache.element_size()
+    span = k_cache.numel() * k_cache.element_size()
+    check(load().da_gather_read_probe(_ptr(k_cache), _ptr(v_cache), _ptr(offsets), offsets.numel(),
+                                      int(row_bytes), int(span), _ptr(sink), int(grid), int(loads_in_flight),
+                                      _stream(offsets)),
+          "da_gather_read_probe")
+
+
 def prefill_tiles_build(m: DaMask, prompt_len: torch.Tensor, n: int, tiles=None) -> torch.Tensor:
     """Tile lists of the keep-set for prefill of len(prompt_len) sequences of
     n tokens (uint8 device buffer in the layout of include/diagattn.h)."""

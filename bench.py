@@ -194,6 +194,27 @@ class DecodeBench:
             self.build(mode)
         self.decode(mode, c)
 
+    def gather_us(self, mode, steps, warmup):
+        """The gather probe on this step's rows: every kept K/V row read once
+        at its byte offset (resolved beforehand through the lists and the
+        block table of each cache copy) and nothing else, cold (rotating
+        over the cache copies), best over GATHER_SHAPES.  Returns
+        (microseconds, (grid, loads in flight))."""
+        torch, da = self.torch, self.da
+        m, cap, count, idx = self.lists[mode]
+        self.build(mode)
+        offs = [da.kept_row_offsets(self.k, self.seqs[c], count, idx, self.bts[c]) for c in range(self.n_copies)]
+        sink = torch.empty(8192, dtype=torch.int32, device=self.dev)
+        best = None
+        for grid, loads in GATHER_SHAPES:
+            def run(c, grid=grid, loads=loads):
+                da.gather_read_probe(self.k, self.v, offs[c], sink, grid, loads_in_flight=loads)
+            us = graph_us(torch, run, self.n_copies, steps, warmup)
+            if best is None or us < best[0]:
+                best = (us, (grid, loads))
+        del offs
+        return best
+
     def burn(self, mode, seconds, path="fused"):
         """Replays graphs of back-to-back steps for `seconds`, untimed: the
         first ~0.1 s of decode steps after the streaming burn-in run up to
@@ -622,6 +643,7 @@ def burn_in(bufs, seconds):
 
 
 PROBE_SHAPES = ((2048, 1), (4096, 1), (1024, 2), (512, 4), (256, 8), (2048, 2), (512, 8))
+GATHER_SHAPES = ((1024, 1), (2048, 1), (4096, 1), (8192, 1), (1024, 2), (2048, 2), (1024, 4))
 
 
 def attainable_read(nbytes, steps=50, warmup=10):
@@ -977,6 +999,9 @@ def main():
     probe_us, probe_grid = attainable_read(kept, K, W)
     log(f"[bench] attainable: a streaming read of the same {kept / 1e6:.1f} MB takes {probe_us:.2f} us "
         f"cold ({kept / probe_us / 1e3:.0f} GB/s, grid/loads {probe_grid})")
+    gather_us, gather_shape = b.gather_us(mode, K, W)
+    log(f"[bench] attainable for the access pattern: a gather of exactly the kept rows takes {gather_us:.2f} us "
+        f"cold ({kept / gather_us / 1e3:.0f} GB/s, grid/loads {gather_shape})")
     value = b.n_q / (us_step * 1e-6)
     traffic = traffic_from_profile(cfg.name)
 
@@ -1080,6 +1105,11 @@ def main():
                                  "GBps": round(eb.kept_bytes(c.modes[0]) / pu / 1e3, 1),
                                  "step_frac_of_attainable": round(
                                      pu / rec[wl.MODE_NAMES[c.modes[0]]]["us_per_step"], 4)}
+            gu, gs = eb.gather_us(c.modes[0], K, W)
+            rec["attainable_gather"] = {"us": round(gu, 3), "grid_loads": list(gs),
+                                        "GBps": round(eb.kept_bytes(c.modes[0]) / gu / 1e3, 1),
+                                        "step_frac_of_attainable": round(
+                                            gu / rec[wl.MODE_NAMES[c.modes[0]]]["us_per_step"], 4)}
             extra[name] = rec
             del eb
             torch.cuda.empty_cache()
@@ -1128,6 +1158,13 @@ def main():
                        "GBps": round(kept / probe_us / 1e3, 1),
                        "frac_of_peak": round(kept / probe_us / 1e3 / HBM_PEAK_GBPS, 4),
                        "step_frac_of_attainable": round(probe_us / us_step, 4)},
+        "attainable_gather": {"what": "gather probe: exactly the kept K/V rows of the step at byte offsets "
+                                      "resolved beforehand (no address chain, no arithmetic); cold, best "
+                                      "(grid, loads in flight) shape",
+                              "us": round(gather_us, 3), "grid_loads": list(gather_shape),
+                              "GBps": round(kept / gather_us / 1e3, 1),
+                              "frac_of_peak": round(kept / gather_us / 1e3 / HBM_PEAK_GBPS, 4),
+                              "step_frac_of_attainable": round(gather_us / us_step, 4)},
         "cpu_baseline": cpu,
         "device": f"{torch.cuda.get_device_properties(0).name} "
                   f"{getattr(torch.cuda.get_device_properties(0), 'gcnArchName', '')}".strip(),

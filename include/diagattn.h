@@ -451,6 +451,24 @@ int da_decode_schedule(const int64_t* cost /* [host] */, int32_t n, int32_t wg_p
 int da_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t grid,
                       int32_t loads_in_flight, void* stream);
 
+/* Measurement: a gather of rows of two buffers, K and V, at n_rows byte
+ * offsets (offsets[n_rows] int64, device) -- given the byte offsets of the
+ * kept K/V rows of a decode step, resolved through its lists and block table
+ * beforehand, it reads exactly what the step must read and nothing else: the
+ * attainable rate of decode's own access pattern (the summary page finds
+ * decode bound by KV-cache reads), without its arithmetic or its address
+ * chain.  Rows of row_bytes (128, 256 or 512) bytes; offsets are clamped
+ * into [0, span_bytes - row_bytes] and rounded down to 16, so no offset
+ * reads outside the buffers (span_bytes: the bytes of K, and of V, from the
+ * base pointers).  `grid` workgroups of 256 threads, `loads_in_flight` (1, 2
+ * or 4) rows of K and of V in flight per lane group; one XOR of the words
+ * read per workgroup to sink[grid] (the XOR over sink is the XOR of every
+ * word of the rows read).  Errors: DA_EINVAL (NULL pointers, sizes,
+ * alignment, grid, loads_in_flight), DA_ENOTSUP (row size). */
+int da_gather_read_probe(const void* k, const void* v, const int64_t* offsets, int64_t n_rows,
+                         int32_t row_bytes, int64_t span_bytes, uint32_t* sink, int32_t grid,
+                         int32_t loads_in_flight, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -184,3 +184,19 @@ def test_product_path_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(_native, "LIB_PATH", "/nonexistent/libdiagattn.so")
     with pytest.raises(RuntimeError, match="missing"):
         _native.load()
+
+
+def test_gather_probe_arguments_are_checked_before_launch():
+    lib = da.load()
+    dummy = ctypes.c_void_p(256)   # never dereferenced: checks fail first
+
+    def gp(row=256, n=10, span=1 << 20, grid=64, loads=2, k=dummy):
+        return lib.da_gather_read_probe(k, dummy, dummy, n, row, span, dummy, grid, loads, None)
+    assert gp(row=192) == -2 and "row" in _native.last_error()
+    assert gp(n=-1) == -1
+    assert gp(grid=0) == -1
+    assert gp(loads=3) == -1 and "loads_in_flight" in _native.last_error()
+    assert gp(span=100) == -1 and "span" in _native.last_error()
+    assert gp(k=ctypes.c_void_p(264)) == -1 and "aligned" in _native.last_error()
+    assert gp(k=None) == -1
+    assert gp(n=0) == 0                  # nothing to read
