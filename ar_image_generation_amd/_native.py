@@ -10,7 +10,9 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdiagattn.so")
+# the in-tree build; DIAGATTN_LIB names another build of the same sources
+# (e.g. the host-AddressSanitizer one of build.py)
+LIB_PATH = os.environ.get("DIAGATTN_LIB") or os.path.join(HERE, "libdiagattn.so")
 
 c_i32, c_i64, c_f32, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 

@@ -1,9 +1,15 @@
 """Builds libdiagattn.so (HIP for gfx950) in-tree with hipcc.
 
     python -m ar_image_generation_amd.build
+    python -m ar_image_generation_amd.build --host-asan DIR
 
 Every call recompiles all sources; objects go to ``_build/`` next to this
-file and the shared library to ``libdiagattn.so`` beside it.
+file and the shared library to ``libdiagattn.so`` beside it.  With
+``--host-asan DIR`` the library is built into DIR instead, its host code
+(argument checks, sizing, the batch schedule, the residency tables)
+instrumented with AddressSanitizer and the device code unchanged; run the
+CPU tests against it with ``DIAGATTN_LIB=DIR/libdiagattn.so`` and the
+sanitizer runtime preloaded (``LD_PRELOAD``).
 """
 from __future__ import annotations
 
@@ -57,21 +63,43 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# host-only AddressSanitizer: each -fsanitize= applies to the host pass alone
+HOST_ASAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, host_asan_dir: str = None) -> str:
+    out_dir, lib = (BUILD, LIB) if host_asan_dir is None else (host_asan_dir, os.path.join(host_asan_dir, "libdiagattn.so"))
+    os.makedirs(out_dir, exist_ok=True)
+    extra = [] if host_asan_dir is None else ["-O1", "-g"] + HOST_ASAN
+
+    def comp(src):
+        if host_asan_dir is None:
+            return _compile(src)
+        obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *[f for f in FLAGS if f != "-O3"], *extra, *EXTRA_FLAGS.get(src, []), "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+        return obj
+
     with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+        objs = list(ex.map(comp, SOURCES))
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *([] if host_asan_dir is None else HOST_ASAN[:2]),
+           *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if len(sys.argv) == 3 and sys.argv[1] == "--host-asan":
+        build(verbose=True, host_asan_dir=os.path.abspath(sys.argv[2]))
+    else:
+        build(verbose=True)
     sys.exit(0)
