@@ -287,6 +287,8 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   // wave: row block rb, key block kq at bit 8w + 4rb + kq -- the block holds
   // a kept pair)
   __shared__ int2 tl[LIST_CAP];
+  static_assert(sizeof(ring) + sizeof(bp) + sizeof(tl) <= 80 * 1024 - 512,
+                "two workgroups a CU: at most 80 KiB of LDS each (with room for the compiler's own)");
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches

@@ -150,7 +150,7 @@ def test_random_masks_and_shapes(seed):
                                           (77, 100, 30, 0, 16, 64), (513, 3, 1000, 7, 16, 128),
                                           (1, 0, 4, 1, 16, 128), (1100, 256, 256, 3, 64, 128),
                                           (260, 260, 64, 3, 32, 64), (700, 31, 2**31 - 1, 8, 64, 128),
-                                          (1030, 0, 160, 5, 80, 128)])
+                                          (1030, 0, 160, 5, 80, 128), (1100, 5, 2100, 3, 1016, 128)])
 def test_row_diagonal_shapes(n, P, W, B, G, hd):
     """Row-diagonal masks at raster widths of 16 to 80 with bands up to 8:
     ragged lengths, prompts longer than the sequence, windows past the
