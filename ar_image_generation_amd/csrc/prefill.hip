@@ -287,8 +287,8 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   // wave: row block rb, key block kq at bit 8w + 4rb + kq -- the block holds
   // a kept pair)
   __shared__ int2 tl[LIST_CAP];
-  static_assert(sizeof(ring) + sizeof(bp) + sizeof(tl) <= 80 * 1024 - 512,
-                "two workgroups a CU: at most 80 KiB of LDS each (with room for the compiler's own)");
+  static_assert(sizeof(ring) + sizeof(bp) + sizeof(tl) <= 80 * 1024 - 32,
+                "two workgroups a CU: at most 80 KiB of LDS each (160 KiB a CU), with a few bytes for the compiler's own");
 
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: scalar branches
@@ -324,7 +324,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
     mine0 = list[2 * t];
     mine1 = list[2 * t + 1];
   }
-  const int P = clampi(a.prompt_len[b], 0, n);
+  const int P = __builtin_amdgcn_readfirstlane(clampi(a.prompt_len[b], 0, n));   // uniform: scalar mask terms
 
   const uint16_t* qb = a.q + b * a.sq[0] + h * a.sq[1];
   const uint16_t* kb = (const uint16_t*)uniform_ptr(a.k + b * a.sk[0] + hk * a.sk[1]);
