@@ -183,9 +183,10 @@ __device__ inline void dma_tile(const void* kbase, const void* vbase, const uint
 //    the diagonal k G of its window, the keys r0 - kG - B .. r0 - kG + 15 + B
 //    (causal: up to r0 - kG + 15), so with that alignment the run starts on a
 //    16-key block of the tile and, for B <= 8, fills at most two blocks.
-// A tile in which every row block needs at most two of the four key blocks
-// is a "half" tile: each wave computes only those two blocks per row block,
-// at half the matrix and softmax work.  The list holds the whole tiles
+// A tile in which every wave's rows (row blocks w and w + 4, 64 rows apart)
+// need at most two of the four key blocks is a "half" tile: each wave
+// computes only those two blocks, shared by its row blocks, at half the
+// matrix, softmax and LDS-read work.  The list holds the whole tiles
 // first, then the half tiles, so that the attention kernel runs them in two
 // loops (the order of the online softmax's steps does not change its
 // result beyond rounding).
@@ -220,14 +221,14 @@ __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
       const bool win = c >= n_pro;
       const int j0 = win ? wb + (c - n_pro) * BN : c * BN;
       uint64_t need = 0, full = 0;
-      bool half = true;                          // every row block needs <= 2 key blocks
+      bool half = true;                          // every wave needs <= 2 key blocks
       if (c < n_pro + n_win) {
-        for (int w = 0; w < NWAVE; ++w)
+        for (int w = 0; w < NWAVE; ++w) {
+          unsigned uni = 0;                        // key blocks any of the wave's rows needs
           for (int rb = 0; rb < RB_MAX; ++rb) {
-            const int rlo = i0 + (w * RB_MAX + rb) * 16;
+            const int rlo = i0 + w * 16 + rb * NWAVE * 16;
             if (rlo > i_last) continue;
             const int rhi = rlo + 15 < i_last ? rlo + 15 : i_last;
-            int nk = 0;
             for (int kq = 0; kq < 4; ++kq) {
               const int jlo = j0 + 16 * kq, jhi = jlo + 15;
               const uint64_t bit = uint64_t(1) << (w * 8 + rb * 4 + kq);
@@ -240,11 +241,12 @@ __global__ void __launch_bounds__(64) prefill_tiles_kernel(PrefillArgs a) {
                 has = jl <= jhi && range_has_kept(rlo, rhi, jl, jhi, P, a.mode, a.W, a.B, a.G);
                 all = false;
               }
-              if (has) { need |= bit; ++nk; }
+              if (has) { need |= bit; uni |= 1u << kq; }
               if (all) full |= bit;
             }
-            half = half && nk <= 2;
           }
+          half = half && __popc(uni) <= 2;
+        }
       }
       const bool keep = need != 0 && half == (pass == 1);
       const uint64_t bal = __ballot(keep);
@@ -330,13 +332,16 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   const uint16_t* kb = (const uint16_t*)uniform_ptr(a.k + b * a.sk[0] + hk * a.sk[1]);
   const uint16_t* vb = (const uint16_t*)uniform_ptr(a.v + b * a.sv[0] + hk * a.sv[1]);
 
-  // ---- this wave's 16*RB query rows; lane lr of block rb holds row
-  // wi0 + 16*rb + lr; its Q^T operand chunks stay in registers
-  const int wi0 = i0 + wave * 16 * RB;
+  // ---- this wave's query rows: blocks w and w + 4 of the tile, 64 rows
+  // apart (RS), so that on a raster width dividing 64 both meet a window
+  // tile's diagonal runs in the same key blocks; lane lr of block rb holds
+  // row wi0 + RS*rb + lr; its Q^T operand chunks stay in registers
+  constexpr int RS = NWAVE * 16;
+  const int wi0 = i0 + wave * 16;
   bf16x8 qv[RB][NC];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const int i = wi0 + 16 * rb + lr;
+    const int i = wi0 + RS * rb + lr;
     const uint16_t* qrow = qb + (int64_t)(i < n ? i : n - 1) * a.sq[2];
 #pragma unroll
     for (int c = 0; c < NC; ++c)
@@ -421,7 +426,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
 
   const int vt_row = 4 * lg + (lr >> 2);
   const int vt_sub = (lr & 3);
-  const int my_i0 = wi0 + lr;          // this lane's row in block 0 (block rb adds 16 rb)
+  const int my_i0 = wi0 + lr;          // this lane's row in block 0 (block rb adds RS rb)
 
   // Keep word of this lane's row in block rb over the tile's keys j0..j0+63
   // (bit c: key j0 + c at distance x - c).  Prompt tiles: the causal bits
@@ -429,7 +434,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   // the prompt end.  A window tile past the prompt, below every row's
   // diagonal and inside every row's window needs only the band pattern.
   auto keep_word = [&](int rb, int j0, bool win, bool inner) __attribute__((always_inline)) -> uint64_t {
-    const int x = my_i0 + 16 * rb - j0;
+    const int x = my_i0 + RS * rb - j0;
     if (!win) {
       if constexpr (MODE == DA_MODE_DENSE) return bit_range(0, x);
       else return bit_range(0, (x < P - j0 - 1 ? x : P - j0 - 1));
@@ -442,13 +447,13 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
     }
   };
 
-  // One step over NQ of the staged tile's 16-key blocks per row block:
-  // blk[rb][..] (all four, or the two holding row block rb's kept pairs).
+  // One step over NQ of the staged tile's 16-key blocks: blk[..] (all four,
+  // or the two holding the wave's kept pairs), shared by its row blocks.
   // S^T = K Q^T (A = K from LDS), masks, online softmax, O^T += V^T P^T
   // over pairs of blocks (A = V^T by transposing LDS reads).  Rows 16
   // apart share the swizzle, so a block's LDS addresses are a per-lane base
   // plus 16 q rows.
-  auto body = [&](auto nq, const uint16_t* st0, const int (&blk)[RB][4], bool masked, int j0, bool win,
+  auto body = [&](auto nq, const uint16_t* st0, const int (&blk)[4], bool masked, int j0, bool win,
                   bool inner) __attribute__((always_inline)) {
     constexpr int NQ = decltype(nq)::value;
     f32x4 sc[RB][NQ];
@@ -459,12 +464,10 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const int pos = (4 * c + lg) ^ swz<CPR>(lr);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st0 + (16 * blk[hq] + lr) * HD + pos * 8);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const int row = 16 * blk[rb][hq] + lr;
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(st0 + row * HD + pos * 8);
+        for (int rb = 0; rb < RB; ++rb)
           sc[rb][hq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qv[rb][c], sc[rb][hq], 0, 0, 0);
-        }
       }
     }
     if (masked) {
@@ -473,7 +476,7 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
         const uint64_t keep = keep_word(rb, j0, win, inner);
 #pragma unroll
         for (int hq = 0; hq < NQ; ++hq) {
-          const uint32_t wd = (uint32_t)(keep >> (16 * blk[rb][hq] + 4 * lg));
+          const uint32_t wd = (uint32_t)(keep >> (16 * blk[hq] + 4 * lg));
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int32_t m = (int32_t)(wd << (31 - r)) >> 31;
@@ -530,16 +533,15 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
         typedef short v8i16 __attribute__((ext_vector_type(8)));
         const int chunk = 2 * nb + (vt_sub >> 1);
         const int lane_off = vt_row * HD + ((chunk ^ swz<CPR>(vt_row)) * 8) + (vt_sub & 1) * 4;
+        const uint16_t* plo = st0 + TILE + 16 * blk[2 * cc] * HD + lane_off;
+        const uint16_t* phi = st0 + TILE + 16 * blk[2 * cc + 1] * HD + lane_off;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
+        const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          const uint16_t* plo = st0 + TILE + 16 * blk[rb][2 * cc] * HD + lane_off;
-          const uint16_t* phi = st0 + TILE + 16 * blk[rb][2 * cc + 1] * HD + lane_off;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(plo));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(phi));
-          const v8i16 w = v8i16{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+        for (int rb = 0; rb < RB; ++rb)
           o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pb[rb][cc], o[rb][nb], 0, 0, 0);
-        }
       }
     }
   };
@@ -573,23 +575,17 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
     const bool win = (ex >> 17) & 1;
     const uint16_t* st0 = ring + ST * 2 * TILE;
     const bool inner = MODE == DA_MODE_ROWDIAG && win && j0 >= P && wi0 - j0 >= BN - 1 &&
-                       wi0 + 16 * RB - 1 - j0 <= W;
+                       wi0 + RS * (RB - 1) + 15 - j0 <= W;
     if constexpr (NQ == 2) {
-      // each row block's (at most) two key blocks holding its kept pairs; a
-      // row block with one takes a second it has no kept pair in
-      int blk[RB][4];
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const unsigned m4 = (need8 >> (4 * rb)) & 0xfu;
-        const int q0 = m4 ? __builtin_ctz(m4) : 0;
-        const unsigned rest = m4 & (m4 - 1);
-        blk[rb][0] = q0;
-        blk[rb][1] = rest ? __builtin_ctz(rest) : (q0 + 1) & 3;
-        blk[rb][2] = blk[rb][3] = 0;
-      }
+      // the (at most) two key blocks holding the wave's kept pairs; with one,
+      // a second it has no kept pair in
+      const unsigned m4 = (need8 | (need8 >> 4)) & 0xfu;
+      const int q0 = m4 ? __builtin_ctz(m4) : 0;
+      const unsigned rest = m4 & (m4 - 1);
+      const int blk[4] = {q0, rest ? __builtin_ctz(rest) : (q0 + 1) & 3, 0, 0};
       body(nq, st0, blk, true, j0, win, inner);
     } else {
-      const int blk[RB][4] = {{0, 1, 2, 3}, {0, 1, 2, 3}};
+      const int blk[4] = {0, 1, 2, 3};
       const bool allfull = (ex >> (18 + wave)) & 1;
       body(nq, st0, blk, !allfull, j0, win, inner);
     }
@@ -614,12 +610,12 @@ __global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2
   run(std::integral_constant<int, 4>{}, 0, n_whole);
   run(std::integral_constant<int, 2>{}, n_whole, cnt);
 
-  // ---- normalise and store: lane holds row wi0+16rb+lr, dims 16nb + 4lg + r
+  // ---- normalise and store: lane holds row wi0+RS*rb+lr, dims 16nb + 4lg + r
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float L = ls[rb];
     L = sum_over_row_groups(L);
-    const int i = wi0 + 16 * rb + lr;
+    const int i = wi0 + RS * rb + lr;
     if (i > i_last) continue;
     const float inv = 1.f / L;
     uint16_t* orow = a.o + b * a.so[0] + h * a.so[1] + (int64_t)i * a.so[2];

@@ -355,11 +355,13 @@ int64_t da_prefill_tiles_bytes(int32_t batch, int32_t n);
  * counting keys below the prompt end only, window tiles keys at or past it
  * -- and for each two 64-bit masks over (wave w, row block rb, key block kq),
  * bit w*8 + rb*4 + kq: the block holds a kept pair / every pair of the block
- * is kept (bits 32..63, waves 4..7, are zero with 4 waves a tile).  Tiles in
- * which some row block needs three or four of the key blocks come first
- * ("whole" tiles), then the tiles in which every row block needs at most two
- * ("half" tiles: only those two are computed).  Layout of `tiles` (16-byte
- * aligned, da_prefill_tiles_bytes long):
+ * is kept (bits 32..63, waves 4..7, are zero with 4 waves a tile); row block
+ * rb of wave w is rows 128 qt + 16 w + 64 rb .. + 15.  Tiles in which some
+ * wave needs three or four of the key blocks come first ("whole" tiles),
+ * then the tiles in which every wave's two row blocks together need at most
+ * two ("half" tiles: only those two are computed, shared by both row
+ * blocks).  Layout of `tiles` (16-byte aligned, da_prefill_tiles_bytes
+ * long):
  *   int32 count[batch][n_qt] = list length | number of whole tiles << 16,
  *         padded to 16 bytes, then
  *   int32 entry[batch][n_qt][max_tiles][8] = {first key, need lo, need hi,

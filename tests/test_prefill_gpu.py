@@ -223,8 +223,8 @@ def test_tile_lists_hold_every_kept_pair_once(mode, n, P, W, B, G):
     (row, key) pair lies in exactly one listed (tile, 16-key block) marked as
     holding a kept pair -- prompt tiles counting keys below the prompt end,
     window tiles keys at or past it -- every block marked wholly kept is, in
-    a half tile each row block marks at most two blocks, and whole tiles come
-    first."""
+    a half tile each wave (row blocks w and w + 4 of the query tile) marks at
+    most two blocks, and whole tiles come first."""
     prompt = [P, min(P, n) // 2]
     m = da.mask(mode, W, B, G)
     tiles = da.prefill_tiles_build(m, torch.as_tensor(prompt, dtype=torch.int32).to(DEV), n)
@@ -237,6 +237,7 @@ def test_tile_lists_hold_every_kept_pair_once(mode, n, P, W, B, G):
         for qt in range(counts.shape[1]):
             cnt, n_whole = int(counts[b, qt]) & 0xffff, int(counts[b, qt]) >> 16
             assert 0 < cnt <= max_tiles and n_whole <= cnt
+
             i0 = 128 * qt
             for e in range(cnt):
                 j0, nlo, nhi, win, flo, fhi = (int(x) for x in ent[b, qt, e, :6])
@@ -244,11 +245,12 @@ def test_tile_lists_hold_every_kept_pair_once(mode, n, P, W, B, G):
                 full = (flo & 0xffffffff) | ((fhi & 0xffffffff) << 32)
                 assert -15 <= j0 < n and need != 0
                 for w in range(4):
+                    if e >= n_whole:
+                        union = ((need >> (8 * w)) | (need >> (8 * w + 4))) & 0xf
+                        assert bin(union).count("1") <= 2, (b, qt, e, w)
                     for rb in range(2):
-                        r0 = i0 + 32 * w + 16 * rb
+                        r0 = i0 + 16 * w + 64 * rb
                         bits = (need >> (8 * w + 4 * rb)) & 0xf
-                        if e >= n_whole:
-                            assert bin(bits).count("1") <= 2, (b, qt, e, w, rb)
                         for kq in range(4):
                             if not (bits >> kq) & 1:
                                 continue
