@@ -1,16 +1,16 @@
 // band_prefill_attn: causal, keep-set-masked attention over whole sequences,
 // bf16 in, fp32 accumulation, on the matrix cores (v_mfma_f32_16x16x32_bf16).
 //
-// Workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
-// two blocks of 16 rows.  The 64-key tiles that hold a kept pair (listed
-// once per query tile by prefill_tiles_kernel) stream K and V into a
-// two-stage LDS ring by direct global->LDS copies, the next tile in flight
-// while the current one is computed.  A workgroup takes at most 80 KiB of
-// LDS, so two share a CU: while one waits at its per-tile barrier the
-// other's matrix work keeps the CU busy.  Scores are
-// computed transposed, S^T = K Q^T (A = K from LDS, B = Q^T from
-// registers), so that the MFMA result gives every lane one query row and
-// four keys of each 16-key block.  That lane-per-row layout is kept for the
+// Workgroup = 4 waves = 128 query rows of one (batch, head); wave w owns
+// the 16-row blocks w and w + 4 (64 rows apart).  The 64-key tiles that hold
+// a kept pair (listed once per query tile by prefill_tiles_kernel) stream K
+// and V into a two-stage LDS ring by direct global->LDS copies, the next
+// tile in flight while the current one is computed.  A workgroup takes at
+// most 80 KiB of LDS, so two share a CU: while one waits at its per-tile
+// barrier the other's matrix work keeps the CU busy.  Scores are computed
+// transposed, S^T = K Q^T (A = K from LDS, B = Q^T from registers), so that
+// the MFMA result gives every lane one query row and four keys of each
+// 16-key block.  That lane-per-row layout is kept for the
 // whole softmax: the running max/sum are per lane (combined over the four
 // lanes of a row by lane swaps), the probabilities P^T are already in the B
 // operand layout of the second product, and the output is accumulated
@@ -20,13 +20,16 @@
 // Sparsity: only listed key tiles are visited.  Keys below the prompt end
 // come in tiles on multiples of 64, keys past it in window tiles aligned so
 // that each 16-row block's kept run on a diagonal starts on a 16-key block
-// of the tile; a wave whose row blocks each hold their kept pairs of a tile
-// in at most two of its four 16-key blocks computes only those two (half
-// the products, exponentials and mask work of the tile).  A wave none of
-// whose rows keeps a key of the tile only takes part in the copies and
-// barriers; a wave whose blocks are all wholly kept applies no mask;
-// otherwise each row gets a 64-bit keep word over the tile's keys (causal,
-// prompt and window bits) and every score keeps its bit or becomes -inf.
+// of the tile.  A tile in which every wave's two row blocks hold their kept
+// pairs in at most two of its four 16-key blocks is computed on those two
+// only (half the products, exponentials and LDS operand reads); with the
+// row blocks 64 rows apart, raster widths dividing 64 make the two row
+// blocks meet the same diagonal runs, so window tiles are such tiles.  A
+// wave none of whose rows keeps a key of the tile only takes part in the
+// copies and barriers; a wave whose blocks are all wholly kept applies no
+// mask; otherwise each row gets a 64-bit keep word over the tile's keys
+// (causal, prompt and window bits) and every score keeps its bit or becomes
+// -inf.
 // (Skipping single 16x16 blocks inside a wave behind uniform branches
 // measured slower: it breaks the interleaving of the unrolled products.)
 // Workgroups are numbered so that all query tiles of one (batch, head)
@@ -58,7 +61,8 @@ struct PrefillArgs {
   float inv_g;                      // 1 / G
 };
 
-// Query tile: NWAVE waves x RB_MAX row blocks of 16 rows; key tile: BN keys.
+// Query tile: NWAVE waves x RB_MAX row blocks of 16 rows (wave w: blocks w,
+// w + NWAVE); key tile: BN keys.
 constexpr int RB_MAX = 2;
 constexpr int NWAVE = 4;
 static_assert(NWAVE * 8 <= 32, "the LDS list keeps 8 full-block bits per wave in 32 bits");
