@@ -954,8 +954,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the decode path is data-parallel over requests "
-              "and heads with no exchange, and this build runs on a single MI355X. "
-              "Run with --gpus 1.", file=sys.stderr)
+              "and heads with no exchange, so a GPU's throughput is its share of the batch; "
+              "multi-GPU runs are not part of this benchmark. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     if args.profile_run:
